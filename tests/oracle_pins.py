@@ -1,0 +1,561 @@
+"""Pins that tie the fp64 oracle to what the pages and the mathematics fix.
+
+Each ``pin_*`` takes an oracle library handle (``oracle.load()`` or a deliberately
+broken build) and raises AssertionError when the oracle disagrees with the pin.
+``test_oracle_pins.py`` runs them on the real oracle; ``test_oracle_mutants.py``
+plants mistakes in copies of the oracle source and checks that some pin catches
+every one of them.
+
+Kinds of pin (none re-types the oracle's formula):
+  * exhaustive codec checks against torch's CPU conversions and the format tables;
+  * hand-derived closed-form cases (tests/golden/hand_cases.json);
+  * brute force: numpy dense masked attention over a de-paged cache;
+  * special cases that reduce to a library routine (torch's scaled_dot_product_attention
+    with a causal or sliding-window mask, in float64 on the CPU);
+  * invariants (page permutation, garbage past counts, index order, GQA expansion,
+    sink as a closed-form factor, block-sparse as a token selection).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+import struct
+
+import numpy as np
+import torch
+
+import oracle
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_cases.json")
+
+
+# ------------------------------------------------------------------ helpers
+
+def dense_keys(cache: W.PagedCache, b: int, layer: int, T: int) -> np.ndarray:
+    """[planes, T, Hkv, D] float64 of positions 0..T-1 of sequence b, read through the
+    page table with torch indexing and decoded by torch's own dtype conversion."""
+    if T == 0:
+        return np.zeros((cache.planes, 0, cache.num_kv_heads, cache.head_dim))
+    pv = cache.pages_view()
+    npg = (T + cache.page_size - 1) // cache.page_size
+    pages = torch.as_tensor(cache.lookup_table[b, :npg].astype(np.int64))
+    x = pv[pages][:, :, layer]                                   # [npg, planes, ps, Hkv, D]
+    x = x.permute(1, 0, 2, 3, 4).reshape(cache.planes, npg * cache.page_size,
+                                         cache.num_kv_heads, cache.head_dim)[:, :T]
+    return x.to(torch.float32).to(torch.float64).numpy()
+
+
+def q64(case) -> np.ndarray:
+    return case.q.to(torch.float32).to(torch.float64).numpy()
+
+
+def masked_softmax_attend(qh, K, V, weight, scale, sink=-math.inf):
+    """Dense masked attention: keys with weight 0 are masked out; weight w>0 counts a
+    key w times. qh [H, D], K/V [T, D] (shared by the H heads)."""
+    S = float(np.float32(scale)) * (qh @ K.T)                    # [H, T]
+    live = weight > 0
+    out = np.zeros((qh.shape[0], V.shape[1]))
+    if not live.any():
+        return out
+    Sl = S[:, live]
+    m = np.maximum(Sl.max(axis=1, keepdims=True), sink)
+    E = weight[live][None, :] * np.exp(Sl - m)
+    Z = E.sum(axis=1, keepdims=True) + np.exp(sink - m)
+    return (E @ V[live]) / Z
+
+
+def brute_qsa(case) -> np.ndarray:
+    """numpy dense masked attention for the index-selected op (multiplicity-weighted mask)."""
+    kv = case.kv
+    G = case.num_q_heads // kv.num_kv_heads
+    off = case.input_row_offsets.astype(np.int64)
+    Wd = case.token_indices.shape[1]
+    qq = q64(case)
+    out = np.zeros(qq.shape)
+    for b in range(case.batch):
+        T = int(kv.cache_lengths[b]) + int(off[b + 1] - off[b])
+        KV = dense_keys(kv, b, case.layer_idx, T)
+        for r in range(off[b], off[b + 1]):
+            n = max(0, min(int(case.counts[r]), Wd))
+            w = np.bincount(case.token_indices[r, :n].astype(np.int64), minlength=T)[:T].astype(np.float64)
+            for g in range(kv.num_kv_heads):
+                hs = slice(g * G, (g + 1) * G)
+                out[r, hs] = masked_softmax_attend(qq[r, hs], KV[0, :, g], KV[1, :, g], w, case.scale)
+    return out
+
+
+def brute_block_sparse(case) -> np.ndarray:
+    kv = case.kv
+    G = case.num_q_heads // kv.num_kv_heads
+    off = case.input_row_offsets.astype(np.int64)
+    pos = case.positions()
+    bs = case.block_size
+    qq = q64(case)
+    out = np.zeros(qq.shape)
+    for b in range(case.batch):
+        T = int(pos[off[b + 1] - 1]) + 1
+        KV = dense_keys(kv, b, case.layer_idx, T)
+        for r in range(off[b], off[b + 1]):
+            for g in range(kv.num_kv_heads):
+                w = np.zeros(T)
+                for blk in case.d_indices[g, r]:
+                    lo = int(blk) * bs
+                    hi = min(lo + bs, int(pos[r]) + 1)
+                    if hi > lo:
+                        w[lo:hi] += 1
+                hs = slice(g * G, (g + 1) * G)
+                out[r, hs] = masked_softmax_attend(qq[r, hs], KV[0, :, g], KV[1, :, g], w, case.scale)
+    return out
+
+
+def brute_latent(case, sink=None) -> np.ndarray:
+    off = case.input_row_offsets.astype(np.int64)
+    pos = case.positions()
+    qq = q64(case)
+    sink = case.attn_sink.astype(np.float64) if sink is None else sink
+    out = np.zeros(qq.shape)
+    for b in range(case.batch):
+        T = int(pos[off[b + 1] - 1]) + 1
+        X = dense_keys(case.kv, b, case.layer_idx, T)[0, :, 0]           # [T, D]
+        E = int(case.comp_indices[off[b]:off[b + 1]].max(initial=-1)) + 1
+        C = dense_keys(case.comp, b, case.layer_idx, E)[0, :, 0]          # [E, D]
+        XC = np.concatenate([X, C], axis=0)
+        for r in range(off[b], off[b + 1]):
+            w = np.zeros(T + E)
+            w[max(0, int(pos[r]) - case.window + 1): int(pos[r]) + 1] = 1
+            ce = case.comp_indices[r]
+            w[T:] += np.bincount(ce[ce >= 0].astype(np.int64), minlength=E)[:E]
+            for h in range(case.num_q_heads):
+                out[r, h] = masked_softmax_attend(qq[r, h][None], XC, XC, w, case.scale, sink[h])[0]
+    return out
+
+
+def assert_close(a, b, tol, what):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    assert np.isfinite(a).all(), what + ": oracle output has non-finite values"
+    err = np.abs(a - b).max() if a.size else 0.0
+    assert err <= tol, "%s: max abs diff %.3e > %.1e" % (what, err, tol)
+
+
+def sdpa64(q, k, v, mask, scale):
+    """torch's scaled_dot_product_attention in float64 on the CPU (library routine)."""
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.as_tensor(q), torch.as_tensor(k), torch.as_tensor(v),
+        attn_mask=torch.as_tensor(mask), scale=float(np.float32(scale))).numpy()
+
+
+def clone_case(case, **kw):
+    import copy
+    c = copy.copy(case)
+    c.kv = copy.copy(case.kv)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+# ------------------------------------------------------------------ small cases
+
+def small_qsa_cases():
+    """A spread of tiny shapes: dtypes, groups, kv heads, layers, padded pages, selections."""
+    return [
+        W.c1_tiny_fp32(),
+        W.make_qsa(name="bf16_g2_h3_pad", seed=11, rows=[2, 1, 4], cache_lengths=[5, 0, 9],
+                   page_size=4, num_layers=3, layer_idx=1, num_kv_heads=3, group=2, head_dim=8,
+                   dtype="bf16", out_dtype="bf16", selection_width=7, selection="uniform_counts",
+                   scale=0.3, spare_pages=2, page_pad=5),
+        W.make_qsa(name="e4m3_g1_h2", seed=12, rows=[3, 2], cache_lengths=[12, 3], page_size=8,
+                   num_layers=2, layer_idx=0, num_kv_heads=2, group=1, head_dim=16, dtype="e4m3",
+                   out_dtype="bf16", selection_width=6, selection="min", scale=0.25, std=0.5),
+        W.make_qsa(name="bf16_recent", seed=13, rows=[6], cache_lengths=[20], page_size=4,
+                   num_layers=1, layer_idx=0, num_kv_heads=1, group=4, head_dim=8, dtype="bf16",
+                   out_dtype="bf16", selection_width=12, selection="recent", recent=4, scale=0.4),
+    ]
+
+
+def small_block_sparse_case(seed=21, rows=None, cache_lengths=(40, 70, 13), topk=3, dtype="e4m3"):
+    return W.make_block_sparse(name="bs_small", seed=seed, cache_lengths=list(cache_lengths), rows=rows,
+                               page_size=8, num_kv_heads=2, group=3, head_dim=16, dtype=dtype,
+                               topk=topk, block_size=4, scale=0.25, std=0.5, num_layers=2, layer_idx=1)
+
+
+def small_latent_case(seed=31, unused=0.3):
+    return W.make_latent(name="lat_small", seed=seed, decode_positions=[40, 13], prefill_positions=[25],
+                         prefill_rows=5, num_heads=3, head_dim=16, dtype="bf16", out_dtype="bf16",
+                         window=6, swa_page_size=4, comp_page_size=4, num_comp=5, comp_ratio=2,
+                         unused_frac=unused, scale=0.25)
+
+
+# ------------------------------------------------------------------ pins: codecs
+
+def pin_bf16_codec_exhaustive(lib):
+    codes = np.arange(65536, dtype=np.uint16)
+    got = oracle.decode("bf16", codes, lib=lib)
+    ref = torch.from_numpy(codes.astype(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all(), "bf16 NaN codes differ"
+    assert (got[~nan] == ref[~nan]).all(), "bf16 decode differs from torch"
+    # format definition, independent of torch: (-1)^s * 2^(e-127) * (1 + m/128), e in 1..254
+    for c in (0x3F80, 0xC000, 0x0001, 0x7F7F, 0x4049, 0x8000, 0x0080):
+        s, e, m = c >> 15, (c >> 7) & 0xFF, c & 0x7F
+        v = (2.0 ** (e - 127)) * (1 + m / 128) if e else (2.0 ** -126) * (m / 128)
+        v = -v if s else v
+        assert got[c] == v, hex(c)
+    assert got[0x7F80] == math.inf and got[0xFF80] == -math.inf
+
+
+def pin_e4m3_codec_exhaustive(lib):
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.decode("e4m3", codes, lib=lib)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert (np.isnan(got) == nan).all(), "e4m3 NaN codes differ"
+    assert (got[~nan] == ref[~nan]).all(), "e4m3 decode differs from torch"
+    table = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+             0x39: 1.125, 0x40: 2.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, v in table.items():
+        assert got[c] == v, (hex(c), got[c], v)
+
+
+def pin_f32_passthrough(lib):
+    x = np.array([0.0, -1.5, 3.25e-40, 1e38, np.inf], np.float32)
+    got = oracle.decode("f32", x, lib=lib)
+    assert (got == x.astype(np.float64)).all()
+
+
+# ------------------------------------------------------------------ pins: golden
+
+def _golden_leaf(spec, D, planes, L, Hkv):
+    n = spec["num_pages"]
+    t = torch.full((n, planes, L, spec["page_size"], Hkv, D), float("nan"), dtype=torch.float32)
+    for key, vals in spec["kv"].items():
+        p, pl, l, s, h = (int(x) for x in key.split(","))
+        t[p, pl, l, s, h] = torch.tensor(vals, dtype=torch.float32)
+    return t
+
+
+def pin_golden_hand_cases(lib):
+    cases = json.load(open(GOLDEN))["cases"]
+    for c in cases:
+        D, Hq = c["head_dim"], c["num_q_heads"]
+        q = torch.tensor(c["q"], dtype=torch.float32)
+        off = np.concatenate([[0], np.cumsum(c["rows"])]).astype(np.uint32)
+        if c["op"] in ("qsa", "block_sparse"):
+            Hkv, L = c["num_kv_heads"], c["num_layers"]
+            blocks = _golden_leaf(c, D, 2, L, Hkv)
+            common = dict(q=q, dtype="f32", input_row_offsets=off, kv_blocks=blocks,
+                          num_pages=c["num_pages"], num_layers=L, page_size=c["page_size"],
+                          num_kv_heads=Hkv, page_stride=-1, cache_lengths=c["cache_lengths"],
+                          kv_lookup_table=np.array(c["lookup_table"]), layer_idx=c["layer_idx"],
+                          scale=c["scale"], lib=lib)
+            if c["op"] == "qsa":
+                got = oracle.sparse_attention(token_indices=np.array(c["token_indices"]),
+                                              counts=np.array(c["counts"]), **common)
+            else:
+                got = oracle.block_sparse_attention(d_indices=np.array(c["d_indices"]),
+                                                    block_size=c["block_size"], **common)
+        else:
+            leaves = {}
+            for name in ("swa", "comp"):
+                sp = c[name]
+                leaves[name] = dict(blocks=_golden_leaf(sp, D, 1, 1, 1), num_pages=sp["num_pages"],
+                                    num_layers=1, page_size=sp["page_size"], page_stride=-1,
+                                    kv_lookup_table=np.array(sp["lookup_table"]),
+                                    cache_lengths=c["cache_lengths"])
+            sink = np.array([float(x) for x in c["attn_sink"]], np.float32)
+            got = oracle.latent_sparse_attention(q=q, dtype="f32", input_row_offsets=off,
+                                                 swa=leaves["swa"], comp=leaves["comp"], layer_idx=0,
+                                                 window=c["window"],
+                                                 comp_indices=np.array(c["comp_indices"]),
+                                                 attn_sink=sink, scale=c["scale"], lib=lib)
+        assert_close(got, np.array(c["expected"]), 1e-15, "golden " + c["name"])
+
+
+# ------------------------------------------------------------------ pins: qsa
+
+def pin_qsa_brute_force(lib):
+    for case in small_qsa_cases():
+        got = oracle.run_case(case, lib=lib)
+        assert_close(got, brute_qsa(case), 1e-12, "qsa brute force " + case.name)
+
+
+def pin_qsa_duplicates_and_count_edges(lib):
+    case = W.c1_tiny_fp32()
+    idx = case.token_indices.copy()
+    cnt = case.counts.copy()
+    idx[1, :4] = [5, 5, 5, 9]                 # duplicates count with multiplicity
+    cnt[1] = 4
+    cnt[2] = 0                                # empty selection -> zero row
+    cnt[3] = -3
+    idx[4, :] = np.arange(16) % 30            # counts > width clamps to width
+    cnt[4] = 99
+    c2 = clone_case(case, token_indices=idx, counts=cnt)
+    got = oracle.run_case(c2, lib=lib)
+    assert (got[2] == 0).all() and (got[3] == 0).all()
+    ref = brute_qsa(c2)
+    assert_close(got, ref, 1e-12, "qsa duplicates/edges")
+
+
+def pin_qsa_counts_one_exact(lib):
+    case = small_qsa_cases()[1]
+    cnt = np.ones_like(case.counts)
+    c2 = clone_case(case, counts=cnt)
+    got = oracle.run_case(c2, lib=lib)
+    kv = case.kv
+    G = case.num_q_heads // kv.num_kv_heads
+    off = case.input_row_offsets
+    for b in range(case.batch):
+        T = int(kv.cache_lengths[b]) + int(off[b + 1] - off[b])
+        KV = dense_keys(kv, b, case.layer_idx, T)
+        for r in range(off[b], off[b + 1]):
+            p = case.token_indices[r, 0]
+            for h in range(case.num_q_heads):
+                assert (got[r, h] == KV[1, p, h // G]).all(), "counts=1 must return the V row exactly"
+
+
+def pin_qsa_scale_zero_mean(lib):
+    case = small_qsa_cases()[2]
+    c2 = clone_case(case, scale=0.0)
+    got = oracle.run_case(c2, lib=lib)
+    kv = case.kv
+    G = case.num_q_heads // kv.num_kv_heads
+    off = case.input_row_offsets
+    for b in range(case.batch):
+        T = int(kv.cache_lengths[b]) + int(off[b + 1] - off[b])
+        KV = dense_keys(kv, b, case.layer_idx, T)
+        for r in range(off[b], off[b + 1]):
+            sel = case.token_indices[r, :case.counts[r]]
+            for h in range(case.num_q_heads):
+                assert_close(got[r, h], KV[1, sel, h // G].mean(axis=0), 1e-14, "scale=0 mean")
+
+
+def pin_qsa_page_permutation(lib):
+    case = small_qsa_cases()[1]
+    base = oracle.run_case(case, lib=lib)
+    rng = np.random.default_rng(99)
+    kv = case.kv
+    perm = rng.permutation(kv.num_pages)                 # old page i moves to perm[i]
+    st = kv.storage.view(kv.num_pages, kv.page_elems)
+    new = torch.empty_like(st)
+    new[torch.as_tensor(perm)] = st
+    import copy
+    kv2 = copy.copy(kv)
+    kv2.storage = new.view(-1)
+    kv2.lookup_table = perm[kv.lookup_table.astype(np.int64)].astype(np.uint32)
+    got = oracle.run_case(clone_case(case, kv=kv2), lib=lib)
+    assert np.array_equal(got, base), "page permutation changed the oracle output"
+
+
+def pin_qsa_garbage_past_counts(lib):
+    case = small_qsa_cases()[0]
+    base = oracle.run_case(case, lib=lib)
+    assert np.isfinite(base).all()
+    # poison: slots past counts name real, unselected positions whose K/V are set to NaN
+    import copy
+    kv = copy.copy(case.kv)
+    kv.storage = case.kv.storage.clone()
+    pv = kv.pages_view()
+    idx = case.token_indices.copy()
+    off = case.input_row_offsets
+    for b in range(case.batch):
+        T = int(kv.cache_lengths[b]) + int(off[b + 1] - off[b])
+        used = set()
+        for r in range(off[b], off[b + 1]):
+            used |= set(case.token_indices[r, :case.counts[r]].tolist())
+        free = [p for p in range(T) if p not in used]
+        for p in free:
+            pv[int(kv.lookup_table[b, p // kv.page_size]), :, case.layer_idx, p % kv.page_size] = float("nan")
+        for r in range(off[b], off[b + 1]):
+            n = case.counts[r]
+            if free:
+                idx[r, n:] = [free[k % len(free)] for k in range(idx.shape[1] - n)]
+    got = oracle.run_case(clone_case(case, kv=kv, token_indices=idx), lib=lib)
+    assert np.array_equal(got, base), "entries past counts influenced the output"
+
+
+def pin_qsa_index_order(lib):
+    case = small_qsa_cases()[1]
+    base = oracle.run_case(case, lib=lib)
+    rng = np.random.default_rng(5)
+    idx = case.token_indices.copy()
+    for r in range(case.total_q):
+        n = case.counts[r]
+        idx[r, :n] = rng.permutation(idx[r, :n])
+    got = oracle.run_case(clone_case(case, token_indices=idx), lib=lib)
+    assert_close(got, base, 1e-12, "index order")
+
+
+def pin_qsa_gqa_expansion(lib):
+    """Repeating each kv head `group` times and running with group 1 gives the same result."""
+    case = small_qsa_cases()[1]
+    kv = case.kv
+    G = case.num_q_heads // kv.num_kv_heads
+    base = oracle.run_case(case, lib=lib)
+    pv = kv.pages_view()
+    rep = pv.repeat_interleave(G, dim=4).contiguous()
+    import copy
+    kv2 = copy.copy(kv)
+    kv2.storage = rep.view(-1)
+    kv2.num_kv_heads = kv.num_kv_heads * G
+    kv2.page_stride = -1
+    got = oracle.run_case(clone_case(case, kv=kv2), lib=lib)
+    assert np.array_equal(got, base), "GQA expansion changed the output"
+
+
+def pin_qsa_full_selection_is_causal_attention(lib):
+    """Selecting every position 0..pos equals dense causal attention (torch SDPA, fp64)."""
+    case = W.make_qsa(name="full", seed=14, rows=[4, 3], cache_lengths=[6, 2], page_size=4,
+                      num_layers=1, layer_idx=0, num_kv_heads=2, group=2, head_dim=8, dtype="bf16",
+                      out_dtype="bf16", selection_width=16, selection="min", scale=0.35)
+    got = oracle.run_case(case, lib=lib)
+    kv = case.kv
+    G = case.num_q_heads // kv.num_kv_heads
+    off = case.input_row_offsets
+    qq = q64(case)
+    for b in range(case.batch):
+        nr = int(off[b + 1] - off[b])
+        T = int(kv.cache_lengths[b]) + nr
+        KV = dense_keys(kv, b, 0, T)
+        k = np.repeat(KV[0].transpose(1, 0, 2), G, axis=0)            # [Hq, T, D]
+        v = np.repeat(KV[1].transpose(1, 0, 2), G, axis=0)
+        qb = qq[off[b]:off[b + 1]].transpose(1, 0, 2)                  # [Hq, nr, D]
+        posr = int(kv.cache_lengths[b]) + np.arange(nr)
+        mask = np.arange(T)[None, :] <= posr[:, None]
+        ref = sdpa64(qb, k, v, mask, case.scale).transpose(1, 0, 2)
+        assert_close(got[off[b]:off[b + 1]], ref, 1e-12, "full selection vs SDPA")
+
+
+# ------------------------------------------------------------------ pins: block-sparse
+
+def pin_block_sparse_brute_force(lib):
+    for case in (small_block_sparse_case(), small_block_sparse_case(seed=22, rows=[3, 1, 2], dtype="bf16")):
+        got = oracle.run_case(case, lib=lib)
+        assert_close(got, brute_block_sparse(case), 1e-12, "block-sparse brute force")
+
+
+def pin_block_sparse_is_token_selection(lib):
+    """Expanding block ids into per-kv-head token lists and running the index-selected op on
+    one-kv-head slices gives bit-identical results."""
+    case = small_block_sparse_case()
+    got = oracle.run_case(case, lib=lib)
+    kv = case.kv
+    G = case.num_q_heads // kv.num_kv_heads
+    pos = case.positions()
+    bs = case.block_size
+    pv = kv.pages_view()
+    for g in range(kv.num_kv_heads):
+        lists = []
+        for r in range(case.total_q):
+            toks = [int(blk) * bs + i for blk in case.d_indices[g, r] for i in range(bs)
+                    if int(blk) * bs + i <= pos[r]]
+            lists.append(toks)
+        Wd = max(len(t) for t in lists)
+        idx = np.full((case.total_q, Wd), -7, np.int32)
+        for r, t in enumerate(lists):
+            idx[r, :len(t)] = t
+        sl = pv[:, :, :, :, g:g + 1].contiguous()
+        out = oracle.sparse_attention(q=case.q[:, g * G:(g + 1) * G].contiguous(), dtype=case.dtype,
+                                      input_row_offsets=case.input_row_offsets, kv_blocks=sl,
+                                      num_pages=kv.num_pages, num_layers=kv.num_layers,
+                                      page_size=kv.page_size, num_kv_heads=1, page_stride=-1,
+                                      cache_lengths=kv.cache_lengths, kv_lookup_table=kv.lookup_table,
+                                      layer_idx=case.layer_idx, token_indices=idx,
+                                      counts=np.array([len(t) for t in lists], np.int32),
+                                      scale=case.scale, lib=lib)
+        assert np.array_equal(out, got[:, g * G:(g + 1) * G]), "block-sparse != token selection"
+
+
+def pin_block_sparse_all_blocks_is_causal(lib):
+    """Listing every block up to the row's position equals dense causal attention (SDPA).
+
+    Row 0 (position 9) also lists block 3 (positions 12..15), which lies wholly after
+    the row and must contribute nothing."""
+    case = W.make_block_sparse(name="bs_all", seed=23, cache_lengths=[9, 15], page_size=8,
+                               num_kv_heads=1, group=2, head_dim=8, dtype="bf16", topk=3,
+                               block_size=4, scale=0.3, std=1.0)
+    di = np.array([[[2, 0, 3, 1], [3, 1, 0, 2]]], np.int32)
+    got = oracle.run_case(clone_case(case, d_indices=di), lib=lib)
+    qq = q64(case)
+    for r, T in ((0, 10), (1, 16)):
+        KV = dense_keys(case.kv, r, 0, T)
+        k = np.repeat(KV[0].transpose(1, 0, 2), 2, axis=0)
+        v = np.repeat(KV[1].transpose(1, 0, 2), 2, axis=0)
+        ref = sdpa64(qq[r:r + 1].transpose(1, 0, 2), k, v, np.ones((1, T), bool),
+                     case.scale).transpose(1, 0, 2)
+        assert_close(got[r:r + 1], ref, 1e-12, "all blocks vs SDPA row %d" % r)
+
+
+# ------------------------------------------------------------------ pins: latent
+
+def pin_latent_brute_force(lib):
+    for case in (small_latent_case(), small_latent_case(seed=32, unused=0.0)):
+        got = oracle.run_case(case, lib=lib)
+        assert_close(got, brute_latent(case), 1e-12, "latent brute force")
+
+
+def pin_latent_window_only_is_sliding_window_attention(lib):
+    """No compressed entries and no sink equals sliding-window causal attention (SDPA)."""
+    case = small_latent_case(seed=33)
+    ci = np.full_like(case.comp_indices, -1)
+    sink = np.full(case.num_q_heads, -np.inf, np.float32)
+    got = oracle.run_case(clone_case(case, comp_indices=ci, attn_sink=sink), lib=lib)
+    off = case.input_row_offsets
+    pos = case.positions()
+    qq = q64(case)
+    for b in range(case.batch):
+        T = int(pos[off[b + 1] - 1]) + 1
+        X = dense_keys(case.kv, b, 0, T)[0, :, 0]
+        pr = pos[off[b]:off[b + 1]]
+        p = np.arange(T)[None, :]
+        mask = (p <= pr[:, None]) & (p > pr[:, None] - case.window)
+        # positions outside every window hold NaN in the leaf; they are masked out, so
+        # zero them for the library routine (0 weight times NaN would still be NaN)
+        X = np.where(np.isnan(X), 0.0, X)
+        x = np.ascontiguousarray(np.broadcast_to(X, (case.num_q_heads, T, X.shape[1])))
+        ref = sdpa64(qq[off[b]:off[b + 1]].transpose(1, 0, 2), x, x, mask, case.scale).transpose(1, 0, 2)
+        assert_close(got[off[b]:off[b + 1]], ref, 1e-12, "window-only vs SDPA")
+
+
+def pin_latent_sink_factor(lib):
+    """out_with_sink = out_without_sink * sigmoid(LSE(scores) - sink), per row and head."""
+    case = small_latent_case(seed=34)
+    nos = np.full(case.num_q_heads, -np.inf, np.float32)
+    with_sink = oracle.run_case(case, lib=lib)
+    without = oracle.run_case(clone_case(case, attn_sink=nos), lib=lib)
+    off = case.input_row_offsets
+    pos = case.positions()
+    qq = q64(case)
+    sc = float(np.float32(case.scale))
+    for b in range(case.batch):
+        T = int(pos[off[b + 1] - 1]) + 1
+        X = dense_keys(case.kv, b, 0, T)[0, :, 0]
+        E = int(case.comp_indices[off[b]:off[b + 1]].max(initial=-1)) + 1
+        C = dense_keys(case.comp, b, 0, E)[0, :, 0]
+        for r in range(off[b], off[b + 1]):
+            keys = [X[p] for p in range(max(0, int(pos[r]) - case.window + 1), int(pos[r]) + 1)]
+            keys += [C[e] for e in case.comp_indices[r] if e >= 0]
+            Kr = np.stack(keys)
+            for h in range(case.num_q_heads):
+                s = sc * (Kr @ qq[r, h])
+                lse = s.max() + math.log(np.exp(s - s.max()).sum())
+                f = 1.0 / (1.0 + math.exp(float(case.attn_sink[h]) - lse))
+                assert_close(with_sink[r, h], without[r, h] * f, 1e-13, "sink factor")
+
+
+def pin_latent_unused_slots_anywhere(lib):
+    """-1 slots are skipped wherever they sit: compacting them to the tail changes nothing."""
+    case = small_latent_case(seed=35, unused=0.4)
+    base = oracle.run_case(case, lib=lib)
+    ci = np.full_like(case.comp_indices, -1)
+    for r in range(case.total_q):
+        v = case.comp_indices[r][case.comp_indices[r] >= 0]
+        ci[r, :len(v)] = v
+    got = oracle.run_case(clone_case(case, comp_indices=ci), lib=lib)
+    assert np.array_equal(got, base)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,56 @@
+"""Plant plausible mistakes in copies of the oracle source (on the CPU) and check that
+the pins catch every one. A mutant that no pin catches would mean the oracle could
+carry that mistake unnoticed."""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_pins as P
+
+SRC = open(os.path.join(os.path.dirname(oracle.__file__), "qsa_oracle.c")).read()
+
+# (name, text in the oracle source, replacement). Leaving the sink out of the running
+# maximum is not listed: softmax is shift-invariant, so that change is an equivalent
+# mutant (it only matters once exp overflows, where both results round to zero).
+MUTANTS = [
+    ("page_from_slot", "p / c->page_size]", "p % c->page_size]"),
+    ("slot_from_page", "int64_t slot = p % c->page_size;", "int64_t slot = p / c->page_size;"),
+    ("kv_head_dropped", "* c->num_kv_heads + g)", "* c->num_kv_heads + 0)"),
+    ("layer_dropped", "(plane * c->num_layers + layer)", "(plane * c->num_layers + 0)"),
+    ("page_stride_ignored", "c->page_stride == -1 ? packed : c->page_stride", "packed"),
+    ("scale_dropped", "s[j] = scale * acc;", "s[j] = acc;"),
+    ("exp_sign_flipped", "double w = exp(s[j] - m);", "double w = exp(m - s[j]);"),
+    ("value_is_key", "out[d] += w * V[j * D + d];", "out[d] += w * K[j * D + d];"),
+    ("q_reversed", "qv[d] = elem(q, dt, (r * Hq + h) * D + d);",
+     "qv[d] = elem(q, dt, (r * Hq + h) * D + (D - 1 - d));"),
+    ("v_from_k_plane", "gather_row(&c, b, p, 1, layer_idx, g, V + j * D)",
+     "gather_row(&c, b, p, 0, layer_idx, g, V + j * D)"),
+    ("counts_ignored", "int64_t n = counts[r] < W ? counts[r] : W;", "int64_t n = W;"),
+    ("counts_off_by_one", "int64_t n = counts[r] < W ? counts[r] : W;",
+     "int64_t n = counts[r] < W ? counts[r] - 1 : W;"),
+    ("causal_clip_off_by_one", "if (p > pos)", "if (p >= pos)"),
+    ("window_off_by_one", "pos - window + 1 > 0 ? pos - window + 1 : 0", "pos - window > 0 ? pos - window : 0"),
+    ("sink_dropped", "double z = exp(sink - m);", "double z = 0.0;"),
+    ("unused_slot_zero_skipped", "if (e >= 0)", "if (e > 0)"),
+    ("bf16_shift", "(uint32_t)h << 16", "(uint32_t)h << 15"),
+    ("e4m3_bias", "ldexp(8.0 + m, e - 10)", "ldexp(8.0 + m, e - 9)"),
+    ("e4m3_subnormal", "ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    ("normalise_dropped", "out[d] /= z;", "out[d] /= 1.0;"),
+    ("max_not_subtracted_consistently", "z += w;", "z += w * 1.0000001;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new, tmp_path):
+    assert SRC.count(old) >= 1, "mutation site vanished: " + old
+    src = tmp_path / ("mut_%s.c" % name)
+    src.write_text(SRC.replace(old, new))
+    lib = oracle.load(oracle.compile_source(str(src), str(tmp_path / ("mut_%s.so" % name))))
+    for pin in P.ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError):
+            return
+    pytest.fail("no pin caught the planted mistake " + name)
