@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark: index-selected sparse GQA over a paged bf16 KV cache, decode shape.
+
+Workload (one step = one call of qsa_sparse_attention = address generation + gather +
+online softmax + split-K combine): 64 sequences with one query row each, cache
+lengths U[1024, 8192], page size 128, 4 layers (layer 2 addressed), 32 q heads over
+8 kv heads, head_dim 128, selection width 2048 with counts = min(2048, pos + 1),
+bf16 in and out, synthetic seeded inputs (seed 2).
+
+Inputs are resident in HBM before timing. To keep the timed steps honest about
+caches, the KV pool is replicated R times at distinct addresses (R page tables
+pointing at disjoint copies) and step k uses copy k mod R, so consecutive steps
+never re-read what the previous one left in L2 or the 256 MiB MALL.
+
+Prints one JSON line: throughput in gathered-KV GB/s (value), query rows/s, the
+fraction of the 8 TB/s HBM peak, a roofline object for the gather kernel timed with
+HIP events around that kernel alone, and the fp64 CPU oracle timed on the host as
+a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "gathered-KV GB/s (% of HBM peak) + query-rows/s, bf16 decode config"
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t pairs from the HIP runtime (the library records them on its stream)."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pairs = []
+        for _ in range(n):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(a)) == 0
+            assert self.hip.hipEventCreate(ctypes.byref(b)) == 0
+            self.pairs.append((a.value, b.value))
+
+    def ms(self, i):
+        t = ctypes.c_float()
+        a, b = self.pairs[i]
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(t), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        assert rc == 0, rc
+        return t.value
+
+    def close(self):
+        for a, b in self.pairs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(a))
+            self.hip.hipEventDestroy(ctypes.c_void_p(b))
+
+
+def replicate(dc, R):
+    """R copies of the KV pool at distinct addresses, one page table per copy."""
+    import copy
+    import torch
+    kv = dc.kv
+    per = kv.blocks.numel()
+    big = torch.empty(per * R, dtype=kv.blocks.dtype, device=kv.blocks.device)
+    reps = []
+    for k in range(R):
+        big[k * per:(k + 1) * per].copy_(kv.blocks)
+        c = copy.copy(kv)
+        c.blocks = big
+        c.num_pages = kv.num_pages * R
+        c.lookup_table = (kv.lookup_table.to(torch.int64) + k * kv.num_pages).to(torch.int32).contiguous()
+        reps.append(c)
+    return big, reps
+
+
+def cpu_baseline(case, budget_s):
+    """The fp64 oracle on the host cores over the whole workload, repeated for about
+    `budget_s` seconds (at least once)."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or oracle.default_threads()
+    oracle.run_case(case, nthreads=threads)          # page in / build
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oracle.run_case(case, nthreads=threads)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / n
+    gb = W.gathered_kv_bytes(case) / 1e9
+    return {"value": round(gb / dt, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "whole workload (%d query rows, %.1f MB gathered K/V) x %d repetitions, "
+                      "fp64 C oracle with OpenMP; %.3f s per call, %.1f query-rows/s"
+                      % (case.total_q, gb * 1e3, n, dt, case.total_q / dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--waves", type=int, default=0)
+    ap.add_argument("--unroll", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run "
+              "the same kernel on its own shard of sequences or kv heads). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_attention_ragged_amd as qsa
+    import workloads as W
+    from workloads import device as D
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    log("generating c2_decode_bf16 (seed 2)")
+    case = W.c2_decode_bf16()
+    gathered = W.gathered_kv_bytes(case)
+    units = int(np.clip(case.counts, 0, case.token_indices.shape[1]).sum())   # (row, key) pairs
+    # per (row, selected key): Hkv * 2 * D * 2 bytes of K/V plus a 4-byte index
+    algo_bytes = units * (case.kv.num_kv_heads * 2 * case.head_dim * 2 + 4)
+    log("to device (%.2f GB pool)" % (case.kv.storage.numel() * 2 / 1e9))
+    dc = D.to_device(case, dev)
+    _, reps = replicate(dc, args.replicas)
+    del dc.kv
+    torch.cuda.synchronize()
+    opts = {"num_splits": args.splits, "waves": args.waves, "unroll": args.unroll}
+    stream = torch.cuda.current_stream(dev)
+    ws_n = D.workspace_size(D.DeviceCase(case, dc.q, dc.row_off, reps[0], token_indices=dc.token_indices,
+                                         counts=dc.counts), opts)
+    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty(dc.q.shape, dtype=torch.bfloat16, device=dev)
+    calls = [D.DeviceCase(case, dc.q, dc.row_off, reps[k], token_indices=dc.token_indices,
+                          counts=dc.counts) for k in range(args.replicas)]
+
+    def step(k):
+        D.run(calls[k % args.replicas], options=opts, out=out, workspace=ws, stream=stream)
+
+    log("warmup %d" % args.warmup)
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    ev = HipEvents(args.steps)
+    log("timing %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        qsa.set_timing_events(*ev.pairs[k])
+        step(k)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    qsa.set_timing_events(None, None)
+    kern_ms = [ev.ms(k) for k in range(args.steps)]
+    ev.close()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    kern_avg = sum(kern_ms) / len(kern_ms)
+
+    # parity of the last timed output on every row (the oracle takes well under a second)
+    import oracle
+    ref = oracle.run_case(case)
+    got = out.float().cpu().double().numpy()
+    max_abs = float(np.abs(got - ref).max())
+
+    value = gathered / (ms_step * 1e-3) / 1e9
+    achieved = algo_bytes / (kern_avg * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "c2_decode_bf16", "batch": case.batch, "query_rows": case.total_q,
+                   "num_q_heads": case.num_q_heads, "num_kv_heads": case.kv.num_kv_heads,
+                   "head_dim": case.head_dim, "page_size": case.kv.page_size,
+                   "num_layers": case.kv.num_layers, "layer_idx": case.layer_idx,
+                   "selection_width": int(case.token_indices.shape[1]), "seed": case.seed,
+                   "kv_pool_replicas": args.replicas, "launch": opts},
+        "query_rows_per_s": round(case.total_q / (ms_step * 1e-3), 1),
+        "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
+        "gathered_kv_bytes_per_step": gathered,
+        "parity_max_abs_vs_oracle": max_abs,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "gather_valu_kernel<bf16, 128, 4, U>",
+                     "kernel_avg_us": round(kern_avg * 1e3, 3),
+                     "algorithmic_bytes_per_launch": algo_bytes},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (~%.0f s)" % args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,213 @@
+/*
+ * qsa.h - C ABI of the MI355X (gfx950) sparse paged attention library.
+ *
+ * Three operations over a ragged batch of query rows and a paged KV cache:
+ *
+ *   qsa_sparse_attention         index-selected sparse GQA: every query row attends
+ *                                to the positions its token_indices row lists
+ *                                ("QSASparseAttentionRaggedPaged", summary, Tensor
+ *                                shapes and execute() Args);
+ *   qsa_block_sparse_attention   block-sparse attention over top-k KV blocks per
+ *                                (kv head, query row) ("Struct_msa_attention_ragged_paged",
+ *                                design notes and Args);
+ *   qsa_latent_sparse_attention  one shared latent head: sliding-window keys plus
+ *                                listed compressed entries plus a per-head sink logit
+ *                                ("latent_sparse_attention_ragged_paged", summary,
+ *                                Parameters and Args).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are DEVICE pointers unless a comment says (host). The caller owns
+ *     every buffer; the library writes only `out` and `workspace`, never
+ *     allocates, frees or synchronises, and reads no device data on the host.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Arguments are checked on the host before anything is launched; a failed
+ *     check returns a non-zero qsa_status and qsa_last_error() describes it
+ *     ("Raises: Error: If the operand shapes disagree with the parameters" on the
+ *     pages becomes a status code here).
+ *   - Row r of sequence b (input_row_offsets[b] <= r < input_row_offsets[b+1]) is
+ *     at position cache_lengths[b] + (r - input_row_offsets[b]); the cache already
+ *     holds positions 0 .. that position. Only block-sparse (causal clip) and latent
+ *     (window) use the position.
+ *   - Query head h reads kv head h / (num_q_heads / num_kv_heads).
+ *   - Device-data contract (not checked on the host): positions and page ids must
+ *     address the cache. The kernels never dereference an entry that does not
+ *     (a position outside [0, max_pages * page_size), a page id >= num_pages): such
+ *     an entry is skipped as if it were not listed.
+ *   - Results are exact softmax attention up to fp32 rounding: fp32 accumulation,
+ *     fp32 or bf16 (round to nearest even) output. A row with no keys is all zeros.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSA_ABI_VERSION 1
+
+/* Element types. QSA_FP8_E4M3 is the OCP 8-bit E4M3 "fn" format (bias 7, max 448,
+ * no infinity), scale-free as the block-sparse page states for its FP8 path. */
+typedef enum { QSA_F32 = 0, QSA_BF16 = 1, QSA_FP8_E4M3 = 2 } qsa_dtype;
+
+typedef enum {
+    QSA_OK = 0,
+    QSA_ERR_NULL = 1,        /* a required pointer is NULL */
+    QSA_ERR_SHAPE = 2,       /* shapes disagree with each other or with the parameters */
+    QSA_ERR_DTYPE = 3,       /* element types disagree or are not accepted here */
+    QSA_ERR_UNSUPPORTED = 4, /* valid but not built: (dtype, group, head_dim) or launch option */
+    QSA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than *_workspace_size reports */
+    QSA_ERR_HIP = 6          /* the HIP runtime refused a launch */
+} qsa_status;
+
+/* One paged cache leaf ("QSASparseAttentionRaggedPaged" Tensor shapes / Args:
+ * kv_blocks, page_stride, cache_lengths, kv_lookup_table, max_cache_length). */
+typedef struct {
+    const void *blocks;      /* [num_pages, num_planes, num_layers, page_size, num_kv_heads, head_dim] */
+    int32_t dtype;           /* qsa_dtype */
+    int32_t reserved0;
+    int64_t num_pages;
+    int64_t num_planes;      /* 2 = K and V planes; 1 = latent leaf (the row is key and value) */
+    int64_t num_layers;
+    int64_t page_size;
+    int64_t num_kv_heads;
+    int64_t head_dim;
+    int64_t page_stride;     /* elements from one page to the next; -1 = packed.  The inside of a
+                                page is always packed [num_planes, num_layers, page_size, Hkv, D]. */
+    const uint32_t *lookup_table; /* [batch, max_pages]: physical page of each logical page */
+    int64_t max_pages;
+    const uint32_t *cache_lengths; /* [batch]: keys cached before this step's rows */
+    uint32_t max_cache_length;     /* (host) max of cache_lengths; a sizing hint only */
+    uint32_t reserved1;
+} qsa_paged_cache;
+
+/* Ragged query rows ("QSASparseAttentionRaggedPaged": q, input_row_offsets,
+ * max_prompt_length). */
+typedef struct {
+    const void *q;           /* [total_q, num_q_heads, head_dim], rows contiguous */
+    int32_t dtype;           /* qsa_dtype; must equal the cache's */
+    int32_t reserved0;
+    int64_t total_q;
+    int64_t num_q_heads;
+    int64_t head_dim;
+    int64_t batch;
+    const uint32_t *input_row_offsets; /* [batch + 1], non-decreasing, last = total_q */
+    uint32_t max_prompt_length;        /* (host) max rows of one sequence; a sizing hint only */
+    uint32_t reserved1;
+} qsa_ragged_q;
+
+/* Launch knobs ("QSASparseAttentionRaggedPaged" execute Parameters: warps per CTA
+ * and keys in flight). Pass NULL, or zeros, for the library's choice. */
+typedef struct {
+    int32_t num_splits;      /* split-K partitions of each row's key list; 0 = automatic */
+    int32_t waves;           /* wavefronts per workgroup; 0 = automatic */
+    int32_t unroll;          /* gathered keys a key team has in flight; 0 = automatic */
+    int32_t reserved;
+} qsa_launch_options;
+
+/* ------------------------------------------------------------------------- */
+/* Index-selected sparse GQA ("QSASparseAttentionRaggedPaged").
+ *
+ * out[r, h, :] = softmax_j(scale * q[r,h,:] . K_j) . V_j over the first
+ * n = min(counts[r], selection_width) entries j of token_indices[r, :], where
+ * position p = token_indices[r, j] of r's sequence is read at page
+ * kv_lookup_table[b, p / page_size], slot p % page_size, plane 0 (K) or 1 (V),
+ * layer layer_idx, kv head h / group. Entries at or past counts[r] are never read.
+ *
+ *   out            [total_q, num_q_heads, head_dim] of out_dtype (QSA_F32 or QSA_BF16)
+ *   q, kv          q->dtype == kv->dtype, in {F32, BF16, FP8_E4M3}; kv->num_planes == 2
+ *   token_indices  [total_q, selection_width] int32, positions within each row's sequence
+ *   counts         [total_q] int32; <= 0 gives a zero row, > selection_width is clamped
+ *   workspace      >= qsa_sparse_attention_workspace_size(...) bytes (may be NULL when that is 0)
+ * Supported now: group in {1, 2, 4} with head_dim in {64, 128, 256} (wavefront dot
+ * products), group in {8, 16} with head_dim 128 (matrix cores).
+ */
+qsa_status qsa_sparse_attention_workspace_size(const qsa_ragged_q *q, const qsa_paged_cache *kv,
+                                               int64_t selection_width,
+                                               const qsa_launch_options *opts, size_t *bytes);
+
+qsa_status qsa_sparse_attention(void *out, int32_t out_dtype, const qsa_ragged_q *q,
+                                const qsa_paged_cache *kv, uint32_t layer_idx,
+                                const int32_t *token_indices, int64_t selection_width,
+                                const int32_t *counts, float scale,
+                                const qsa_launch_options *opts, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------- */
+/* Block-sparse top-k attention ("Struct_msa_attention_ragged_paged").
+ *
+ * For row r at position pos and kv head g the keys are the positions
+ * block_size * t + i (0 <= i < block_size) of every listed block t in
+ * d_indices[g, r, 0:topk] that are <= pos; each q head of group g attends to them.
+ *
+ *   out        [total_q, num_q_heads, head_dim] bf16 (always, as the page states)
+ *   q, kv      BF16 or FP8_E4M3, same type; FP32 accumulation; no dequant scales
+ *   d_indices  [num_kv_heads, total_q, topk] int32 block ids
+ *   block_size must divide kv->page_size
+ *   cache_row_offsets, msa_scalar_args: optional (may be NULL) hints from the page's
+ *   argument list; the result does not depend on them.
+ */
+qsa_status qsa_block_sparse_attention_workspace_size(const qsa_ragged_q *q, const qsa_paged_cache *kv,
+                                                     int64_t topk, int64_t block_size,
+                                                     const qsa_launch_options *opts, size_t *bytes);
+
+qsa_status qsa_block_sparse_attention(void *out, const qsa_ragged_q *q, const qsa_paged_cache *kv,
+                                      uint32_t layer_idx, const int32_t *d_indices, int64_t topk,
+                                      int64_t block_size, float scale,
+                                      const uint32_t *cache_row_offsets,
+                                      const uint32_t *msa_scalar_args,
+                                      const qsa_launch_options *opts, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------- */
+/* Latent window + compressed + sink attention ("latent_sparse_attention_ragged_paged").
+ *
+ * Row r at position pos (from swa->cache_lengths) attends to the window rows at
+ * positions max(0, pos - window + 1) .. pos of the token-paged leaf `swa` and to the
+ * compressed rows at entries comp_indices[r, t] >= 0 of the entry-paged leaf `comp`
+ * (-1 marks an unused slot, anywhere in the row). Each latent row is both key and
+ * value. Head h adds attn_sink[h] (not multiplied by scale) to the softmax
+ * denominator with a zero value row.
+ *
+ *   out           [total_q, num_q_heads, head_dim] of out_dtype (F32 or BF16)
+ *   swa, comp     num_planes == 1, num_kv_heads == 1, head_dim == q->head_dim, same dtype as q
+ *   comp_indices  [total_q, num_comp] int32
+ *   attn_sink     [num_q_heads] float32 (-inf = no sink for that head)
+ */
+qsa_status qsa_latent_sparse_attention_workspace_size(const qsa_ragged_q *q, int64_t window,
+                                                      int64_t num_comp,
+                                                      const qsa_launch_options *opts,
+                                                      size_t *bytes);
+
+qsa_status qsa_latent_sparse_attention(void *out, int32_t out_dtype, const qsa_ragged_q *q,
+                                       const qsa_paged_cache *swa, const qsa_paged_cache *comp,
+                                       uint32_t layer_idx, int64_t window,
+                                       const int32_t *comp_indices, int64_t num_comp,
+                                       const float *attn_sink, float scale,
+                                       const qsa_launch_options *opts, void *workspace,
+                                       size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------- */
+/* Text describing the last non-OK status returned on the calling thread. */
+const char *qsa_last_error(void);
+
+/* QSA_ABI_VERSION of the built library. */
+int32_t qsa_abi_version(void);
+
+/* sizeof() of the ABI structs as built: 0 = qsa_paged_cache, 1 = qsa_ragged_q,
+ * 2 = qsa_launch_options; 0 for any other value. Lets bindings check their layout. */
+size_t qsa_struct_size(int32_t which);
+
+/* Profiling hook for the calling thread: when both are non-NULL, each later call on
+ * this thread records `start` (a hipEvent_t) on its stream right before its main
+ * gather kernel and `stop` right after it, so the caller can time that kernel alone.
+ * Pass NULLs to stop. */
+void qsa_set_timing_events(void *start, void *stop);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

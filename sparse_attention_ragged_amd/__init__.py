@@ -1,0 +1,307 @@
+"""Python binding of the MI355X sparse paged attention library (libqsa.so).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels
+behind the C ABI declared in ``include/qsa.h``. PyTorch supplies device memory and
+the current stream. There is no fallback path: if the built library is missing the
+import fails, and the functions refuse CPU tensors.
+
+Entry points (same names as the C ABI, without the ``qsa_`` prefix):
+
+* ``sparse_attention`` - index-selected sparse GQA over a paged KV cache
+  ("QSASparseAttentionRaggedPaged");
+* ``block_sparse_attention`` - top-k KV blocks per (kv head, row), bf16 output
+  ("Struct_msa_attention_ragged_paged");
+* ``latent_sparse_attention`` - one latent head: sliding window + listed compressed
+  entries + per-head sink ("latent_sparse_attention_ragged_paged").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqsa.so")
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}
+CODE_DTYPE = {v: k for k, v in DTYPE_CODE.items()}
+STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL", 2: "QSA_ERR_SHAPE", 3: "QSA_ERR_DTYPE",
+          4: "QSA_ERR_UNSUPPORTED", 5: "QSA_ERR_WORKSPACE", 6: "QSA_ERR_HIP"}
+
+# Every function declared in include/qsa.h.
+EXPORTS = (
+    "qsa_sparse_attention_workspace_size", "qsa_sparse_attention",
+    "qsa_block_sparse_attention_workspace_size", "qsa_block_sparse_attention",
+    "qsa_latent_sparse_attention_workspace_size", "qsa_latent_sparse_attention",
+    "qsa_last_error", "qsa_abi_version", "qsa_struct_size", "qsa_set_timing_events",
+)
+
+
+class QsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (STATUS.get(status, status), message))
+        self.status = status
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("blocks", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("num_pages", ctypes.c_int64), ("num_planes", ctypes.c_int64),
+                ("num_layers", ctypes.c_int64), ("page_size", ctypes.c_int64),
+                ("num_kv_heads", ctypes.c_int64), ("head_dim", ctypes.c_int64),
+                ("page_stride", ctypes.c_int64), ("lookup_table", ctypes.c_void_p),
+                ("max_pages", ctypes.c_int64), ("cache_lengths", ctypes.c_void_p),
+                ("max_cache_length", ctypes.c_uint32), ("reserved1", ctypes.c_uint32)]
+
+
+class _Ragged(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("total_q", ctypes.c_int64), ("num_q_heads", ctypes.c_int64),
+                ("head_dim", ctypes.c_int64), ("batch", ctypes.c_int64),
+                ("input_row_offsets", ctypes.c_void_p), ("max_prompt_length", ctypes.c_uint32),
+                ("reserved1", ctypes.c_uint32)]
+
+
+class LaunchOptions(ctypes.Structure):
+    """Launch knobs: split-K partitions, wavefronts per workgroup, keys in flight (0 = auto)."""
+    _fields_ = [("num_splits", ctypes.c_int32), ("waves", ctypes.c_int32),
+                ("unroll", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libqsa.so is not built (%s); run sparse_attention_ragged_amd/build.py "
+                          "or __graft_entry__.build()" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    pc, pr, po = ctypes.POINTER(_Cache), ctypes.POINTER(_Ragged), ctypes.POINTER(LaunchOptions)
+    lib.qsa_sparse_attention_workspace_size.argtypes = [pr, pc, I64, po, ctypes.POINTER(SZ)]
+    lib.qsa_sparse_attention.argtypes = [P, I32, pr, pc, ctypes.c_uint32, P, I64, P, F, po, P, SZ, P]
+    lib.qsa_block_sparse_attention_workspace_size.argtypes = [pr, pc, I64, I64, po, ctypes.POINTER(SZ)]
+    lib.qsa_block_sparse_attention.argtypes = [P, pr, pc, ctypes.c_uint32, P, I64, I64, F, P, P, po,
+                                               P, SZ, P]
+    lib.qsa_latent_sparse_attention_workspace_size.argtypes = [pr, I64, I64, po, ctypes.POINTER(SZ)]
+    lib.qsa_latent_sparse_attention.argtypes = [P, I32, pr, pc, pc, ctypes.c_uint32, I64, P, I64, P, F,
+                                                po, P, SZ, P]
+    for name in ("qsa_sparse_attention_workspace_size", "qsa_sparse_attention",
+                 "qsa_block_sparse_attention_workspace_size", "qsa_block_sparse_attention",
+                 "qsa_latent_sparse_attention_workspace_size", "qsa_latent_sparse_attention"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.qsa_last_error.restype = ctypes.c_char_p
+    lib.qsa_abi_version.restype = I32
+    lib.qsa_struct_size.argtypes = [I32]
+    lib.qsa_struct_size.restype = SZ
+    lib.qsa_set_timing_events.argtypes = [P, P]
+    lib.qsa_set_timing_events.restype = None
+    for i, st in enumerate((_Cache, _Ragged, LaunchOptions)):
+        if lib.qsa_struct_size(i) != ctypes.sizeof(st):
+            raise ImportError("ABI mismatch: %s is %d bytes in libqsa.so, %d here"
+                              % (st.__name__, lib.qsa_struct_size(i), ctypes.sizeof(st)))
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != 0:
+        raise QsaError(status, lib.qsa_last_error().decode(errors="replace"))
+
+
+@dataclass
+class PagedCache:
+    """Device view of one paged cache leaf (all tensors on the GPU).
+
+    ``blocks`` holds [num_pages, num_planes, num_layers, page_size, num_kv_heads, head_dim]
+    elements, pages ``page_stride`` elements apart (-1 = packed). ``lookup_table``
+    [batch, max_pages] and ``cache_lengths`` [batch] are 32-bit integer tensors whose
+    bits are read as uint32.
+    """
+    blocks: torch.Tensor
+    num_pages: int
+    num_planes: int
+    num_layers: int
+    page_size: int
+    num_kv_heads: int
+    head_dim: int
+    page_stride: int
+    lookup_table: torch.Tensor
+    cache_lengths: torch.Tensor
+    max_cache_length: int = 0
+
+    def _c(self) -> _Cache:
+        _need_gpu(self.blocks, self.lookup_table, self.cache_lengths)
+        _need_i32(self.lookup_table, self.cache_lengths)
+        return _Cache(self.blocks.data_ptr(), DTYPE_CODE[self.blocks.dtype], 0, self.num_pages,
+                      self.num_planes, self.num_layers, self.page_size, self.num_kv_heads,
+                      self.head_dim, self.page_stride, self.lookup_table.data_ptr(),
+                      self.lookup_table.shape[1], self.cache_lengths.data_ptr(),
+                      self.max_cache_length, 0)
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("sparse_attention_ragged_amd needs device tensors (got a CPU tensor)")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _need_i32(*ts):
+    for t in ts:
+        if t is not None and t.dtype not in (torch.int32, torch.uint32):
+            raise ValueError("index tensors must be 32-bit integers, got %s" % t.dtype)
+
+
+def _ragged(q: torch.Tensor, input_row_offsets: torch.Tensor, max_prompt_length: int) -> _Ragged:
+    _need_gpu(q, input_row_offsets)
+    _need_i32(input_row_offsets)
+    if q.dim() != 3:
+        raise ValueError("q must be [total_q, num_q_heads, head_dim]")
+    return _Ragged(q.data_ptr(), DTYPE_CODE[q.dtype], 0, q.shape[0], q.shape[1], q.shape[2],
+                   input_row_offsets.numel() - 1, input_row_offsets.data_ptr(), max_prompt_length, 0)
+
+
+def _opts(options):
+    if options is None:
+        return None
+    if isinstance(options, LaunchOptions):
+        return ctypes.byref(options)
+    o = LaunchOptions(options.get("num_splits", 0), options.get("waves", 0), options.get("unroll", 0), 0)
+    return ctypes.byref(o)
+
+
+def _stream(q: torch.Tensor, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    elif workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError("workspace too small: %d bytes needed" % nbytes)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _out(q, out_dtype, out):
+    if out is None:
+        return torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    _need_gpu(out)
+    if out.shape != q.shape or out.dtype != out_dtype:
+        raise ValueError("out must be %s of %s" % (tuple(q.shape), out_dtype))
+    return out
+
+
+def sparse_attention_workspace_size(q, input_row_offsets, kv: PagedCache, selection_width: int,
+                                    options=None, max_prompt_length: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    rq = _ragged(q, input_row_offsets, max_prompt_length)
+    ck = kv._c()
+    _check(lib.qsa_sparse_attention_workspace_size(ctypes.byref(rq), ctypes.byref(ck), selection_width,
+                                                   _opts(options), ctypes.byref(n)))
+    return n.value
+
+
+def sparse_attention(q, input_row_offsets, kv: PagedCache, layer_idx: int, token_indices, counts,
+                     scale: float, *, out_dtype=None, max_prompt_length: int = 0, options=None,
+                     out=None, workspace=None, stream=None) -> torch.Tensor:
+    """Index-selected sparse GQA; returns out [total_q, num_q_heads, head_dim]."""
+    out_dtype = out_dtype or (q.dtype if q.dtype != torch.float8_e4m3fn else torch.bfloat16)
+    _need_gpu(token_indices, counts)
+    _need_i32(token_indices, counts)
+    rq = _ragged(q, input_row_offsets, max_prompt_length)
+    ck = kv._c()
+    o = _opts(options)
+    n = ctypes.c_size_t(0)
+    W = token_indices.shape[1] if token_indices.dim() == 2 else 0
+    _check(lib.qsa_sparse_attention_workspace_size(ctypes.byref(rq), ctypes.byref(ck), W, o,
+                                                   ctypes.byref(n)))
+    ws, wsb = _workspace(n.value, q.device, workspace)
+    out = _out(q, out_dtype, out)
+    _check(lib.qsa_sparse_attention(out.data_ptr(), DTYPE_CODE[out_dtype], ctypes.byref(rq),
+                                    ctypes.byref(ck), layer_idx, token_indices.data_ptr(), W,
+                                    counts.data_ptr(), scale, o,
+                                    ws.data_ptr() if ws is not None else None, wsb, _stream(q, stream)))
+    return out
+
+
+def block_sparse_attention_workspace_size(q, input_row_offsets, kv: PagedCache, topk: int,
+                                          block_size: int, options=None) -> int:
+    n = ctypes.c_size_t(0)
+    rq = _ragged(q, input_row_offsets, 0)
+    ck = kv._c()
+    _check(lib.qsa_block_sparse_attention_workspace_size(ctypes.byref(rq), ctypes.byref(ck), topk,
+                                                         block_size, _opts(options), ctypes.byref(n)))
+    return n.value
+
+
+def block_sparse_attention(q, input_row_offsets, kv: PagedCache, layer_idx: int, d_indices,
+                           block_size: int, scale: float, *, max_prompt_length: int = 0,
+                           cache_row_offsets=None, msa_scalar_args=None, options=None, out=None,
+                           workspace=None, stream=None) -> torch.Tensor:
+    """Block-sparse top-k attention; d_indices [num_kv_heads, total_q, topk]; bf16 output."""
+    _need_gpu(d_indices, cache_row_offsets, msa_scalar_args)
+    _need_i32(d_indices)
+    rq = _ragged(q, input_row_offsets, max_prompt_length)
+    ck = kv._c()
+    o = _opts(options)
+    topk = d_indices.shape[2]
+    n = ctypes.c_size_t(0)
+    _check(lib.qsa_block_sparse_attention_workspace_size(ctypes.byref(rq), ctypes.byref(ck), topk,
+                                                         block_size, o, ctypes.byref(n)))
+    ws, wsb = _workspace(n.value, q.device, workspace)
+    out = _out(q, torch.bfloat16, out)
+    _check(lib.qsa_block_sparse_attention(
+        out.data_ptr(), ctypes.byref(rq), ctypes.byref(ck), layer_idx, d_indices.data_ptr(), topk,
+        block_size, scale, cache_row_offsets.data_ptr() if cache_row_offsets is not None else None,
+        msa_scalar_args.data_ptr() if msa_scalar_args is not None else None, o,
+        ws.data_ptr() if ws is not None else None, wsb, _stream(q, stream)))
+    return out
+
+
+def latent_sparse_attention_workspace_size(q, input_row_offsets, window: int, num_comp: int,
+                                           options=None) -> int:
+    n = ctypes.c_size_t(0)
+    rq = _ragged(q, input_row_offsets, 0)
+    _check(lib.qsa_latent_sparse_attention_workspace_size(ctypes.byref(rq), window, num_comp,
+                                                          _opts(options), ctypes.byref(n)))
+    return n.value
+
+
+def latent_sparse_attention(q, input_row_offsets, swa: PagedCache, comp: PagedCache, layer_idx: int,
+                            window: int, comp_indices, attn_sink, scale: float, *, out_dtype=None,
+                            max_prompt_length: int = 0, options=None, out=None, workspace=None,
+                            stream=None) -> torch.Tensor:
+    """Latent window + compressed + sink attention; returns out [total_q, num_q_heads, head_dim]."""
+    out_dtype = out_dtype or (q.dtype if q.dtype != torch.float8_e4m3fn else torch.bfloat16)
+    _need_gpu(comp_indices, attn_sink)
+    _need_i32(comp_indices)
+    if attn_sink.dtype != torch.float32:
+        raise ValueError("attn_sink must be float32")
+    rq = _ragged(q, input_row_offsets, max_prompt_length)
+    cs, cc = swa._c(), comp._c()
+    o = _opts(options)
+    num_comp = comp_indices.shape[1]
+    n = ctypes.c_size_t(0)
+    _check(lib.qsa_latent_sparse_attention_workspace_size(ctypes.byref(rq), window, num_comp, o,
+                                                          ctypes.byref(n)))
+    ws, wsb = _workspace(n.value, q.device, workspace)
+    out = _out(q, out_dtype, out)
+    _check(lib.qsa_latent_sparse_attention(
+        out.data_ptr(), DTYPE_CODE[out_dtype], ctypes.byref(rq), ctypes.byref(cs), ctypes.byref(cc),
+        layer_idx, window, comp_indices.data_ptr(), num_comp, attn_sink.data_ptr(), scale, o,
+        ws.data_ptr() if ws is not None else None, wsb, _stream(q, stream)))
+    return out
+
+
+def set_timing_events(start, stop) -> None:
+    """Record two hipEvent_t handles (ints) around the main gather kernel of later calls
+    on this thread; pass (None, None) to stop."""
+    lib.qsa_set_timing_events(start, stop)

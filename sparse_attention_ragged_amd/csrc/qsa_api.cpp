@@ -1,0 +1,312 @@
+// extern "C" entry points declared in include/qsa.h: check arguments on the host,
+// plan the launch, fill the parameter block and hand it to the kernel launchers.
+// No HIP headers here; all device work goes through the launchers.
+#include <cmath>
+#include <cstring>
+
+#include "qsa_host.hpp"
+
+namespace qsa {
+const char *last_error_text();
+}
+
+using namespace qsa;
+
+namespace {
+
+thread_local void *t_ev_start = nullptr;
+thread_local void *t_ev_stop = nullptr;
+
+void fill_common(GatherParams &p, void *out, int32_t out_dtype, const qsa_ragged_q *q,
+                 int64_t num_kv_heads, uint32_t layer, float scale, const Plan &plan, void *ws)
+{
+    std::memset(&p, 0, sizeof p);
+    p.out = out;
+    p.out_dtype = out_dtype;
+    p.dtype = q->dtype;
+    p.q = q->q;
+    p.total_q = q->total_q;
+    p.num_q_heads = (int32_t)q->num_q_heads;
+    p.num_kv_heads = (int32_t)num_kv_heads;
+    p.head_dim = (int32_t)q->head_dim;
+    p.group = (int32_t)(q->num_q_heads / num_kv_heads);
+    p.batch = (int32_t)q->batch;
+    p.layer = (int32_t)layer;
+    p.row_off = q->input_row_offsets;
+    p.scale_log2 = scale * 1.44269504088896340736f;
+    p.num_splits = plan.num_splits;
+    p.waves = plan.waves;
+    p.unroll = plan.unroll;
+    p.split_keys = plan.split_keys;
+    if (plan.num_splits > 1) {
+        p.ws_acc = static_cast<float *>(ws);
+        p.ws_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + plan.ws_ml_offset);
+    }
+}
+
+qsa_status run(const GatherParams &p, const Plan &plan, void *stream)
+{
+    if (p.total_q == 0)
+        return QSA_OK;
+    int err = 0;
+    if (t_ev_start && t_ev_stop)
+        err = record_event(t_ev_start, stream);
+    if (!err)
+        err = plan.mfma ? launch_gather_mfma(p, stream) : launch_gather_valu(p, stream);
+    if (!err && t_ev_start && t_ev_stop)
+        err = record_event(t_ev_stop, stream);
+    if (!err && plan.num_splits > 1)
+        err = launch_splitk_combine(p, stream);
+    if (err)
+        return fail(QSA_ERR_HIP, "HIP launch failed: %s", hip_error_text(err));
+    return QSA_OK;
+}
+
+qsa_status check_out(void *out, int32_t out_dtype, const qsa_ragged_q *q)
+{
+    if (q->total_q > 0 && !out)
+        return fail(QSA_ERR_NULL, "out is NULL");
+    if (out_dtype != QSA_F32 && out_dtype != QSA_BF16)
+        return fail(QSA_ERR_DTYPE, "out_dtype must be QSA_F32 or QSA_BF16");
+    return QSA_OK;
+}
+
+qsa_status check_workspace(const Plan &plan, void *ws, size_t bytes)
+{
+    if (plan.ws_bytes > 0 && (!ws || bytes < plan.ws_bytes))
+        return fail(QSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", plan.ws_bytes,
+                    bytes, ws ? "" : " (NULL)");
+    if (plan.ws_bytes > 0 && ((uintptr_t)ws & 15u))
+        return fail(QSA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    return QSA_OK;
+}
+
+qsa_status sparse_plan(const qsa_ragged_q *q, const qsa_paged_cache *kv, int64_t W,
+                       const qsa_launch_options *opts, Plan *plan)
+{
+    qsa_status s = check_cache(kv, "kv", 2);
+    if (s == QSA_OK)
+        s = check_q(q, kv, true);
+    if (s == QSA_OK && W < 0)
+        s = fail(QSA_ERR_SHAPE, "selection_width must be >= 0");
+    if (s == QSA_OK)
+        s = plan_gather(q, kv->num_kv_heads, q->dtype, W, 1, opts, plan);
+    return s;
+}
+
+qsa_status block_plan(const qsa_ragged_q *q, const qsa_paged_cache *kv, int64_t topk,
+                      int64_t block_size, const qsa_launch_options *opts, Plan *plan)
+{
+    qsa_status s = check_cache(kv, "kv", 2);
+    if (s == QSA_OK)
+        s = check_q(q, kv, true);
+    if (s == QSA_OK && q->dtype != QSA_BF16 && q->dtype != QSA_FP8_E4M3)
+        s = fail(QSA_ERR_DTYPE, "block-sparse attention takes BF16 or FP8_E4M3 q and cache");
+    if (s == QSA_OK && topk < 1)
+        s = fail(QSA_ERR_SHAPE, "topk must be >= 1");
+    if (s == QSA_OK && (block_size < 1 || kv->page_size % block_size != 0))
+        s = fail(QSA_ERR_SHAPE, "block_size %lld must be >= 1 and divide page_size %lld",
+                 (long long)block_size, (long long)kv->page_size);
+    if (s == QSA_OK && topk * block_size > (int64_t(1) << 30))
+        s = fail(QSA_ERR_SHAPE, "topk * block_size out of range");
+    if (s == QSA_OK)
+        s = plan_gather(q, kv->num_kv_heads, q->dtype, topk * block_size, block_size, opts, plan);
+    return s;
+}
+
+qsa_status latent_plan(const qsa_ragged_q *q, int64_t window, int64_t num_comp,
+                       const qsa_launch_options *opts, Plan *plan)
+{
+    if (!q)
+        return fail(QSA_ERR_NULL, "q descriptor is NULL");
+    if (window < 1)
+        return fail(QSA_ERR_SHAPE, "window must be >= 1");
+    if (num_comp < 0)
+        return fail(QSA_ERR_SHAPE, "num_comp must be >= 0");
+    if (window + num_comp > (int64_t(1) << 30))
+        return fail(QSA_ERR_SHAPE, "window + num_comp out of range");
+    return plan_gather(q, 1, q->dtype, window + num_comp, 1, opts, plan);
+}
+
+}  // namespace
+
+extern "C" {
+
+qsa_status qsa_sparse_attention_workspace_size(const qsa_ragged_q *q, const qsa_paged_cache *kv,
+                                               int64_t selection_width,
+                                               const qsa_launch_options *opts, size_t *bytes)
+{
+    clear_error();
+    if (!bytes)
+        return fail(QSA_ERR_NULL, "bytes is NULL");
+    Plan plan;
+    qsa_status s = sparse_plan(q, kv, selection_width, opts, &plan);
+    *bytes = s == QSA_OK ? plan.ws_bytes : 0;
+    return s;
+}
+
+qsa_status qsa_sparse_attention(void *out, int32_t out_dtype, const qsa_ragged_q *q,
+                                const qsa_paged_cache *kv, uint32_t layer_idx,
+                                const int32_t *token_indices, int64_t selection_width,
+                                const int32_t *counts, float scale,
+                                const qsa_launch_options *opts, void *workspace,
+                                size_t workspace_bytes, void *stream)
+{
+    clear_error();
+    Plan plan;
+    qsa_status s = sparse_plan(q, kv, selection_width, opts, &plan);
+    if (s != QSA_OK)
+        return s;
+    if ((s = check_out(out, out_dtype, q)) != QSA_OK)
+        return s;
+    if (layer_idx >= kv->num_layers)
+        return fail(QSA_ERR_SHAPE, "layer_idx %u >= num_layers %lld", layer_idx,
+                    (long long)kv->num_layers);
+    if (q->total_q > 0 && (!counts || (selection_width > 0 && !token_indices)))
+        return fail(QSA_ERR_NULL, "token_indices and counts are required");
+    if (!std::isfinite(scale))
+        return fail(QSA_ERR_SHAPE, "scale must be finite");
+    if ((s = check_workspace(plan, workspace, workspace_bytes)) != QSA_OK)
+        return s;
+    GatherParams p;
+    fill_common(p, out, out_dtype, q, kv->num_kv_heads, layer_idx, scale, plan, workspace);
+    p.kv = cache_addr(kv, layer_idx);
+    p.cache_lengths = kv->cache_lengths;
+    p.list_kind = KEYS_TOKEN_INDICES;
+    p.indices = token_indices;
+    p.counts = counts;
+    p.width = selection_width;
+    return run(p, plan, stream);
+}
+
+qsa_status qsa_block_sparse_attention_workspace_size(const qsa_ragged_q *q, const qsa_paged_cache *kv,
+                                                     int64_t topk, int64_t block_size,
+                                                     const qsa_launch_options *opts, size_t *bytes)
+{
+    clear_error();
+    if (!bytes)
+        return fail(QSA_ERR_NULL, "bytes is NULL");
+    Plan plan;
+    qsa_status s = block_plan(q, kv, topk, block_size, opts, &plan);
+    *bytes = s == QSA_OK ? plan.ws_bytes : 0;
+    return s;
+}
+
+qsa_status qsa_block_sparse_attention(void *out, const qsa_ragged_q *q, const qsa_paged_cache *kv,
+                                      uint32_t layer_idx, const int32_t *d_indices, int64_t topk,
+                                      int64_t block_size, float scale,
+                                      const uint32_t *cache_row_offsets,
+                                      const uint32_t *msa_scalar_args,
+                                      const qsa_launch_options *opts, void *workspace,
+                                      size_t workspace_bytes, void *stream)
+{
+    (void)cache_row_offsets;
+    (void)msa_scalar_args;
+    clear_error();
+    Plan plan;
+    qsa_status s = block_plan(q, kv, topk, block_size, opts, &plan);
+    if (s != QSA_OK)
+        return s;
+    if ((s = check_out(out, QSA_BF16, q)) != QSA_OK)
+        return s;
+    if (layer_idx >= kv->num_layers)
+        return fail(QSA_ERR_SHAPE, "layer_idx %u >= num_layers %lld", layer_idx,
+                    (long long)kv->num_layers);
+    if (q->total_q > 0 && !d_indices)
+        return fail(QSA_ERR_NULL, "d_indices is required");
+    if (!std::isfinite(scale))
+        return fail(QSA_ERR_SHAPE, "scale must be finite");
+    if ((s = check_workspace(plan, workspace, workspace_bytes)) != QSA_OK)
+        return s;
+    GatherParams p;
+    fill_common(p, out, QSA_BF16, q, kv->num_kv_heads, layer_idx, scale, plan, workspace);
+    p.kv = cache_addr(kv, layer_idx);
+    p.cache_lengths = kv->cache_lengths;
+    p.list_kind = KEYS_BLOCKS;
+    p.block_size = (int32_t)block_size;
+    p.indices = d_indices;
+    p.width = topk;
+    return run(p, plan, stream);
+}
+
+qsa_status qsa_latent_sparse_attention_workspace_size(const qsa_ragged_q *q, int64_t window,
+                                                      int64_t num_comp,
+                                                      const qsa_launch_options *opts,
+                                                      size_t *bytes)
+{
+    clear_error();
+    if (!bytes)
+        return fail(QSA_ERR_NULL, "bytes is NULL");
+    Plan plan;
+    qsa_status s = latent_plan(q, window, num_comp, opts, &plan);
+    *bytes = s == QSA_OK ? plan.ws_bytes : 0;
+    return s;
+}
+
+qsa_status qsa_latent_sparse_attention(void *out, int32_t out_dtype, const qsa_ragged_q *q,
+                                       const qsa_paged_cache *swa, const qsa_paged_cache *comp,
+                                       uint32_t layer_idx, int64_t window,
+                                       const int32_t *comp_indices, int64_t num_comp,
+                                       const float *attn_sink, float scale,
+                                       const qsa_launch_options *opts, void *workspace,
+                                       size_t workspace_bytes, void *stream)
+{
+    clear_error();
+    qsa_status s = check_cache(swa, "swa", 1);
+    if (s == QSA_OK)
+        s = check_cache(comp, "comp", 1);
+    if (s != QSA_OK)
+        return s;
+    if (swa->num_kv_heads != 1 || comp->num_kv_heads != 1)
+        return fail(QSA_ERR_SHAPE, "latent leaves hold one head (num_kv_heads must be 1)");
+    if (comp->dtype != swa->dtype || comp->head_dim != swa->head_dim)
+        return fail(QSA_ERR_SHAPE, "swa and comp leaves must share dtype and head_dim");
+    if ((s = check_q(q, swa, false)) != QSA_OK)
+        return s;
+    Plan plan;
+    if ((s = latent_plan(q, window, num_comp, opts, &plan)) != QSA_OK)
+        return s;
+    if ((s = check_out(out, out_dtype, q)) != QSA_OK)
+        return s;
+    if (layer_idx >= swa->num_layers || layer_idx >= comp->num_layers)
+        return fail(QSA_ERR_SHAPE, "layer_idx %u out of range", layer_idx);
+    if (q->total_q > 0 && ((num_comp > 0 && !comp_indices) || !attn_sink))
+        return fail(QSA_ERR_NULL, "comp_indices and attn_sink are required");
+    if (!std::isfinite(scale))
+        return fail(QSA_ERR_SHAPE, "scale must be finite");
+    if ((s = check_workspace(plan, workspace, workspace_bytes)) != QSA_OK)
+        return s;
+    GatherParams p;
+    fill_common(p, out, out_dtype, q, 1, layer_idx, scale, plan, workspace);
+    p.kv = cache_addr(swa, layer_idx);
+    p.comp = cache_addr(comp, layer_idx);
+    p.cache_lengths = swa->cache_lengths;
+    p.list_kind = KEYS_LATENT;
+    p.indices = comp_indices;
+    p.width = num_comp;
+    p.window = window;
+    p.sink = attn_sink;
+    return run(p, plan, stream);
+}
+
+const char *qsa_last_error(void) { return last_error_text(); }
+
+int32_t qsa_abi_version(void) { return QSA_ABI_VERSION; }
+
+size_t qsa_struct_size(int32_t which)
+{
+    switch (which) {
+    case 0: return sizeof(qsa_paged_cache);
+    case 1: return sizeof(qsa_ragged_q);
+    case 2: return sizeof(qsa_launch_options);
+    default: return 0;
+    }
+}
+
+void qsa_set_timing_events(void *start, void *stop)
+{
+    t_ev_start = start;
+    t_ev_stop = stop;
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Internal host-side interface of the library: launch parameter blocks, the
+// validation/planning functions (pure C++, no HIP headers) and the kernel
+// launchers implemented in the .hip translation units.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "qsa.h"
+
+namespace qsa {
+
+// Thread-local error text behind qsa_last_error().
+qsa_status fail(qsa_status code, const char *fmt, ...);
+void clear_error();
+
+// Addressing of one paged cache leaf, in elements. The element offset of
+// (page, plane, layer, slot, kv head, d) is
+//   page * page_stride + plane * plane_stride + layer_off + slot * slot_stride + head * D + d.
+struct CacheAddr {
+    const void *blocks;
+    const uint32_t *lut;
+    int64_t page_stride;
+    int64_t plane_stride;   // num_layers * page_size * Hkv * D
+    int64_t layer_off;      // layer * page_size * Hkv * D
+    int64_t slot_stride;    // Hkv * D
+    int64_t max_pages;
+    int64_t num_pages;
+    int32_t page_size;
+    int32_t page_shift;     // log2(page_size) when a power of two, else -1
+};
+
+// Key-list kinds the gather kernels walk for one (row, kv head).
+enum KeyList : int32_t {
+    KEYS_TOKEN_INDICES = 0,  // token_indices[r, 0:min(counts[r], W)]
+    KEYS_BLOCKS = 1,         // block ids d_indices[g, r, 0:topk], block_size keys each, clipped at pos
+    KEYS_LATENT = 2,         // window positions then comp_indices[r, :] >= 0
+};
+
+struct GatherParams {
+    void *out;
+    int32_t out_dtype;
+    int32_t dtype;
+    const void *q;
+    int64_t total_q;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t group;
+    int32_t batch;
+    int32_t layer;
+    const uint32_t *row_off;
+    const uint32_t *cache_lengths;   // positions (block-sparse, latent)
+    CacheAddr kv;                    // K/V leaf, or the window leaf for latent
+    CacheAddr comp;                  // compressed leaf (latent only)
+    int32_t list_kind;
+    int32_t block_size;
+    const int32_t *indices;          // token_indices / d_indices / comp_indices
+    const int32_t *counts;           // token-index counts (KEYS_TOKEN_INDICES)
+    int64_t width;                   // W, topk or num_comp
+    int64_t window;                  // latent window
+    const float *sink;               // latent sink logits or NULL
+    float scale_log2;                // scale * log2(e)
+    int32_t num_splits;
+    int32_t waves;
+    int32_t unroll;
+    int64_t split_keys;              // keys per split (in key-list units)
+    float *ws_acc;                   // [S, total_q, Hq, D] when num_splits > 1
+    float *ws_ml;                    // [S, total_q, Hq, 2]
+};
+
+struct Plan {
+    bool mfma;
+    int32_t num_splits;
+    int32_t waves;
+    int32_t unroll;
+    int64_t key_capacity;   // upper bound of keys per (row, kv head)
+    int64_t split_keys;
+    size_t ws_bytes;
+    size_t ws_ml_offset;
+};
+
+// Validation + planning (qsa_plan.cpp). They never touch the device.
+qsa_status check_cache(const qsa_paged_cache *c, const char *what, int64_t planes);
+qsa_status check_q(const qsa_ragged_q *q, const qsa_paged_cache *c, bool same_heads_as_cache);
+qsa_status plan_gather(const qsa_ragged_q *q, int64_t num_kv_heads, int32_t dtype,
+                       int64_t key_capacity, int64_t split_unit, const qsa_launch_options *opts,
+                       Plan *plan);
+CacheAddr cache_addr(const qsa_paged_cache *c, uint32_t layer);
+
+// Launchers (qsa_*.hip). Return a hipError_t value (0 = success).
+int launch_gather_valu(const GatherParams &p, void *stream);
+int launch_gather_mfma(const GatherParams &p, void *stream);
+int launch_splitk_combine(const GatherParams &p, void *stream);
+int record_event(void *event, void *stream);
+const char *hip_error_text(int err);
+
+// Which (dtype, group, head_dim) combinations have a built kernel.
+bool valu_supported(int32_t dtype, int32_t group, int32_t head_dim);
+bool mfma_supported(int32_t dtype, int32_t group, int32_t head_dim);
+
+}  // namespace qsa

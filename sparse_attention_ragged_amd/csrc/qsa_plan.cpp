@@ -1,0 +1,186 @@
+// Host-side argument checks and the split-K launch plan. Pure C++: nothing here
+// touches the device, so every check can be exercised without a GPU.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "qsa_host.hpp"
+
+namespace qsa {
+
+namespace {
+thread_local std::string g_error;
+
+// Workgroups a launch should provide to keep all 256 compute units of an MI355X
+// busy with several resident workgroups each (8 XCDs x 32 CUs).
+constexpr int64_t kTargetWorkgroups = 256 * 8;
+// A split shorter than this many keys spends more on its prologue/epilogue than on
+// gathering.
+constexpr int64_t kMinKeysPerSplit = 128;
+constexpr int32_t kMaxSplits = 64;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+}  // namespace
+
+qsa_status fail(qsa_status code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return code;
+}
+
+void clear_error() { g_error.clear(); }
+
+const char *last_error_text() { return g_error.c_str(); }
+
+static bool valid_dtype(int32_t d) { return d == QSA_F32 || d == QSA_BF16 || d == QSA_FP8_E4M3; }
+
+int64_t elem_bytes(int32_t d) { return d == QSA_F32 ? 4 : d == QSA_BF16 ? 2 : 1; }
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+qsa_status check_cache(const qsa_paged_cache *c, const char *what, int64_t planes)
+{
+    if (!c)
+        return fail(QSA_ERR_NULL, "%s: cache descriptor is NULL", what);
+    if (!c->blocks || !c->lookup_table || !c->cache_lengths)
+        return fail(QSA_ERR_NULL, "%s: blocks, lookup_table and cache_lengths are required", what);
+    if (!valid_dtype(c->dtype))
+        return fail(QSA_ERR_DTYPE, "%s: unknown dtype %d", what, c->dtype);
+    if (c->num_pages < 1 || c->num_layers < 1 || c->page_size < 1 || c->num_kv_heads < 1 ||
+        c->head_dim < 1 || c->max_pages < 1)
+        return fail(QSA_ERR_SHAPE, "%s: num_pages, num_layers, page_size, num_kv_heads, head_dim "
+                                   "and max_pages must be >= 1", what);
+    if (c->num_planes != planes)
+        return fail(QSA_ERR_SHAPE, "%s: num_planes is %lld, expected %lld", what,
+                    (long long)c->num_planes, (long long)planes);
+    if (c->page_size > (1 << 30) || c->max_pages > (int64_t(1) << 31) ||
+        c->num_pages > (int64_t(1) << 32))
+        return fail(QSA_ERR_SHAPE, "%s: page_size, max_pages or num_pages out of range", what);
+    int64_t packed = c->num_planes * c->num_layers * c->page_size * c->num_kv_heads * c->head_dim;
+    if (c->page_stride != -1 && c->page_stride < packed)
+        return fail(QSA_ERR_SHAPE, "%s: page_stride %lld is smaller than a packed page (%lld)", what,
+                    (long long)c->page_stride, (long long)packed);
+    // every K/V row is fetched with 16-byte loads
+    const int64_t eb = elem_bytes(c->dtype);
+    const int64_t stride = c->page_stride == -1 ? packed : c->page_stride;
+    if (!aligned16(c->blocks) || (c->head_dim * eb) % 16 != 0 || (stride * eb) % 16 != 0)
+        return fail(QSA_ERR_SHAPE, "%s: blocks, head_dim rows and page_stride must keep 16-byte "
+                                   "alignment", what);
+    return QSA_OK;
+}
+
+qsa_status check_q(const qsa_ragged_q *q, const qsa_paged_cache *c, bool same_heads_as_cache)
+{
+    if (!q)
+        return fail(QSA_ERR_NULL, "q descriptor is NULL");
+    if (!q->input_row_offsets)
+        return fail(QSA_ERR_NULL, "input_row_offsets is required");
+    if (q->total_q < 0 || q->batch < 1 || q->num_q_heads < 1 || q->head_dim < 1)
+        return fail(QSA_ERR_SHAPE, "q: total_q >= 0, batch >= 1, num_q_heads >= 1, head_dim >= 1");
+    if (q->total_q > 0 && !q->q)
+        return fail(QSA_ERR_NULL, "q data pointer is NULL");
+    if (q->total_q > (int64_t(1) << 31) - 1 || q->batch > (int64_t(1) << 31) - 1 ||
+        q->num_q_heads > 65536)
+        return fail(QSA_ERR_SHAPE, "q: total_q, batch or num_q_heads out of range");
+    if (q->dtype != c->dtype)
+        return fail(QSA_ERR_DTYPE, "q dtype %d differs from the cache dtype %d", q->dtype, c->dtype);
+    if (q->head_dim != c->head_dim)
+        return fail(QSA_ERR_SHAPE, "q head_dim %lld differs from the cache head_dim %lld",
+                    (long long)q->head_dim, (long long)c->head_dim);
+    if (q->total_q > 0 && !aligned16(q->q))
+        return fail(QSA_ERR_SHAPE, "q must be 16-byte aligned");
+    if (same_heads_as_cache && q->num_q_heads % c->num_kv_heads != 0)
+        return fail(QSA_ERR_SHAPE, "num_q_heads %lld is not a multiple of num_kv_heads %lld",
+                    (long long)q->num_q_heads, (long long)c->num_kv_heads);
+    return QSA_OK;
+}
+
+// Split plan for a gather launch: grid = total_q x num_kv_heads x num_splits
+// workgroups. Each (row, kv head) key list of at most `key_capacity` keys is cut
+// into num_splits contiguous ranges of split_keys keys (a multiple of split_unit).
+// With more than one split every workgroup writes an (m, l, acc) partial to the
+// workspace and a combine kernel merges them; with one split the gather kernel
+// writes the output itself.
+qsa_status plan_gather(const qsa_ragged_q *q, int64_t num_kv_heads, int32_t dtype,
+                       int64_t key_capacity, int64_t split_unit, const qsa_launch_options *opts,
+                       Plan *plan)
+{
+    const int64_t group = q->num_q_heads / num_kv_heads;
+    plan->mfma = group >= 8;
+    const bool built = plan->mfma ? mfma_supported(dtype, (int32_t)group, (int32_t)q->head_dim)
+                                  : valu_supported(dtype, (int32_t)group, (int32_t)q->head_dim);
+    if (!built)
+        return fail(QSA_ERR_UNSUPPORTED,
+                    "no kernel built for dtype %d, group %lld, head_dim %lld", dtype,
+                    (long long)group, (long long)q->head_dim);
+    qsa_launch_options o = {0, 0, 0, 0};
+    if (opts)
+        o = *opts;
+    if (o.num_splits < 0 || o.num_splits > kMaxSplits)
+        return fail(QSA_ERR_UNSUPPORTED, "num_splits must be in [0, %d]", kMaxSplits);
+    if (o.waves < 0 || o.waves > 8 || (o.waves & (o.waves - 1)))
+        return fail(QSA_ERR_UNSUPPORTED, "waves must be 0 (automatic) or 1, 2, 4, 8");
+    if (!(o.unroll == 0 || o.unroll == 2 || o.unroll == 4 || o.unroll == 8))
+        return fail(QSA_ERR_UNSUPPORTED, "unroll must be 0 (automatic), 2, 4 or 8");
+    plan->waves = o.waves ? o.waves : 4;
+    plan->unroll = o.unroll ? o.unroll : 4;
+    plan->key_capacity = key_capacity;
+
+    const int64_t cap = key_capacity > 0 ? key_capacity : 1;
+    const int64_t items = q->total_q * num_kv_heads;
+    int64_t splits = o.num_splits;
+    if (splits == 0) {
+        splits = items > 0 ? ceil_div(kTargetWorkgroups, items) : 1;
+        int64_t by_len = ceil_div(cap, kMinKeysPerSplit);
+        if (splits > by_len)
+            splits = by_len;
+        if (splits > kMaxSplits)
+            splits = kMaxSplits;
+        if (splits < 1)
+            splits = 1;
+    }
+    int64_t unit = split_unit > 0 ? split_unit : 1;
+    int64_t sk = ceil_div(ceil_div(cap, splits), unit) * unit;
+    splits = ceil_div(cap, sk);   // drop splits that would start past the capacity
+    if (splits < 1)
+        splits = 1;
+    plan->num_splits = (int32_t)splits;
+    plan->split_keys = sk;
+    plan->ws_bytes = 0;
+    plan->ws_ml_offset = 0;
+    if (splits > 1) {
+        size_t rows_heads = (size_t)q->total_q * (size_t)q->num_q_heads;
+        size_t acc = (size_t)splits * rows_heads * (size_t)q->head_dim * sizeof(float);
+        acc = (acc + 255) & ~(size_t)255;
+        plan->ws_ml_offset = acc;
+        plan->ws_bytes = acc + (size_t)splits * rows_heads * 2 * sizeof(float);
+    }
+    return QSA_OK;
+}
+
+CacheAddr cache_addr(const qsa_paged_cache *c, uint32_t layer)
+{
+    CacheAddr a;
+    const int64_t slab = c->page_size * c->num_kv_heads * c->head_dim;
+    a.blocks = c->blocks;
+    a.lut = c->lookup_table;
+    a.page_stride = c->page_stride == -1 ? c->num_planes * c->num_layers * slab : c->page_stride;
+    a.plane_stride = c->num_layers * slab;
+    a.layer_off = (int64_t)layer * slab;
+    a.slot_stride = c->num_kv_heads * c->head_dim;
+    a.max_pages = c->max_pages;
+    a.num_pages = c->num_pages;
+    a.page_size = (int32_t)c->page_size;
+    a.page_shift = -1;
+    for (int s = 0; s < 31; ++s)
+        if ((int64_t(1) << s) == c->page_size)
+            a.page_shift = s;
+    return a;
+}
+
+}  // namespace qsa

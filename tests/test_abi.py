@@ -1,0 +1,155 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, its struct
+layouts match the binding, and host-side argument checks return the documented
+status codes before anything is launched (no GPU is touched by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+
+@pytest.fixture(scope="module")
+def qsa():
+    import sparse_attention_ragged_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(qsa):
+    names = declared_functions()
+    assert set(names) == set(qsa.EXPORTS), names
+    raw = ctypes.CDLL(qsa.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_abi_version_and_struct_sizes(qsa):
+    assert qsa.lib.qsa_abi_version() == 1
+    assert qsa.lib.qsa_struct_size(0) == ctypes.sizeof(qsa._Cache) == 104
+    assert qsa.lib.qsa_struct_size(1) == ctypes.sizeof(qsa._Ragged) == 64
+    assert qsa.lib.qsa_struct_size(2) == ctypes.sizeof(qsa.LaunchOptions) == 16
+    assert qsa.lib.qsa_struct_size(7) == 0
+
+
+# Host buffers stand in for device pointers: every call below must fail its host checks
+# before any launch, so no pointer is ever dereferenced.
+BUF = ctypes.create_string_buffer(4096 + 16)
+P = (ctypes.addressof(BUF) + 15) & ~15
+
+
+def cache(**kw):
+    from sparse_attention_ragged_amd import _Cache
+    d = dict(blocks=P, dtype=1, reserved0=0, num_pages=4, num_planes=2, num_layers=2, page_size=16,
+             num_kv_heads=2, head_dim=128, page_stride=-1, lookup_table=P, max_pages=4,
+             cache_lengths=P, max_cache_length=10, reserved1=0)
+    d.update(kw)
+    return _Cache(**d)
+
+
+def ragged(**kw):
+    from sparse_attention_ragged_amd import _Ragged
+    d = dict(q=P, dtype=1, reserved0=0, total_q=3, num_q_heads=8, head_dim=128, batch=2,
+             input_row_offsets=P, max_prompt_length=2, reserved1=0)
+    d.update(kw)
+    return _Ragged(**d)
+
+
+def call_qsa(qsa, q=None, kv=None, layer=0, W=16, out=P, out_dtype=1, ws=None, wsb=0, opts=None,
+             scale=0.1, idx=P, counts=P):
+    q = q or ragged()
+    kv = kv or cache()
+    return qsa.lib.qsa_sparse_attention(out, out_dtype, ctypes.byref(q), ctypes.byref(kv), layer, idx, W,
+                                        counts, scale, ctypes.byref(opts) if opts else None, ws, wsb, None)
+
+
+def msg(qsa):
+    return qsa.lib.qsa_last_error().decode()
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(q_kw=dict(dtype=0)), 3),                      # q dtype != cache dtype
+    (dict(kv_kw=dict(num_kv_heads=3)), 2),              # 8 q heads not a multiple of 3
+    (dict(kv_kw=dict(head_dim=64)), 2),                 # head_dim mismatch
+    (dict(layer=2), 2),                                 # layer_idx >= num_layers
+    (dict(kv_kw=dict(page_stride=100)), 2),             # stride below a packed page
+    (dict(kv_kw=dict(num_planes=1)), 2),                # K/V cache needs two planes
+    (dict(kv_kw=dict(blocks=0)), 1),                    # NULL blocks
+    (dict(kv_kw=dict(blocks=P + 2)), 2),                # misaligned blocks
+    (dict(out=0), 1),                                   # NULL out
+    (dict(out_dtype=2), 3),                             # e4m3 output is not offered
+    (dict(idx=0), 1),                                   # NULL token_indices
+    (dict(W=-1), 2),                                    # negative width
+    (dict(scale=float("nan")), 2),                      # non-finite scale
+    (dict(q_kw=dict(num_q_heads=48), kv_kw=dict(num_kv_heads=2)), 4),   # group 24 not built
+    (dict(q_kw=dict(head_dim=96), kv_kw=dict(head_dim=96)), 4),         # head_dim 96 not built
+])
+def test_validation_errors(qsa, case, status):
+    q = ragged(**case.get("q_kw", {}))
+    kv = cache(**case.get("kv_kw", {}))
+    args = {k: v for k, v in case.items() if k not in ("q_kw", "kv_kw")}
+    assert call_qsa(qsa, q=q, kv=kv, **args) == status, msg(qsa)
+    assert msg(qsa)
+
+
+def test_workspace_checks(qsa):
+    q, kv = ragged(), cache()
+    n = ctypes.c_size_t(0)
+    o = qsa.LaunchOptions(4, 0, 0, 0)
+    assert qsa.lib.qsa_sparse_attention_workspace_size(ctypes.byref(q), ctypes.byref(kv), 64,
+                                                       ctypes.byref(o), ctypes.byref(n)) == 0
+    # 4 splits x 3 rows x 8 heads x (128 acc + 2) fp32, acc padded to 256 bytes
+    acc = 4 * 3 * 8 * 128 * 4
+    assert n.value == ((acc + 255) // 256) * 256 + 4 * 3 * 8 * 2 * 4
+    assert call_qsa(qsa, opts=o, W=64) == 5 and "workspace" in msg(qsa)
+    assert call_qsa(qsa, opts=o, W=64, ws=P, wsb=16) == 5
+    one = qsa.LaunchOptions(1, 0, 0, 0)
+    assert qsa.lib.qsa_sparse_attention_workspace_size(ctypes.byref(q), ctypes.byref(kv), 64,
+                                                       ctypes.byref(one), ctypes.byref(n)) == 0
+    assert n.value == 0
+
+
+@pytest.mark.parametrize("opts", [(65, 0, 0, 0), (0, 3, 0, 0), (0, 16, 0, 0), (0, 0, 3, 0), (-1, 0, 0, 0)])
+def test_bad_launch_options(qsa, opts):
+    assert call_qsa(qsa, opts=qsa.LaunchOptions(*opts)) == 4, msg(qsa)
+
+
+def test_block_sparse_checks(qsa):
+    q, kv = ragged(), cache()
+    f = qsa.lib.qsa_block_sparse_attention
+    call = lambda **k: f(k.get("out", P), ctypes.byref(k.get("q", q)), ctypes.byref(k.get("kv", kv)),
+                         k.get("layer", 0), k.get("idx", P), k.get("topk", 4), k.get("bs", 8), 0.1,
+                         None, None, None, None, 0, None)
+    assert call(bs=5) == 2            # block size must divide the page size
+    assert call(topk=0) == 2
+    assert call(q=ragged(dtype=0), kv=cache(dtype=0)) == 3     # fp32 is not offered here
+    assert call(idx=0) == 1
+
+
+def test_latent_checks(qsa):
+    q = ragged(num_q_heads=16, head_dim=512)
+    swa = cache(num_planes=1, num_kv_heads=1, head_dim=512, num_layers=1)
+    comp = cache(num_planes=1, num_kv_heads=1, head_dim=512, num_layers=1)
+    f = qsa.lib.qsa_latent_sparse_attention
+    call = lambda **k: f(P, 1, ctypes.byref(k.get("q", q)), ctypes.byref(k.get("swa", swa)),
+                         ctypes.byref(k.get("comp", comp)), 0, k.get("window", 128), P, 64,
+                         k.get("sink", P), 0.1, None, None, 0, None)
+    assert call(window=0) == 2
+    assert call(swa=cache(num_planes=2, num_kv_heads=1, head_dim=512)) == 2
+    assert call(comp=cache(num_planes=1, num_kv_heads=2, head_dim=512, num_layers=1)) == 2
+    assert call(sink=0) in (1, 4)     # NULL sink (or an unbuilt shape) is refused
+
+
+def test_binding_refuses_cpu_tensors(qsa):
+    import torch
+    q = torch.zeros(2, 4, 64)
+    with pytest.raises(ValueError):
+        qsa.sparse_attention(q, torch.zeros(2, dtype=torch.int32), None, 0, torch.zeros(2, 4, dtype=torch.int32),
+                             torch.zeros(2, dtype=torch.int32), 0.1)

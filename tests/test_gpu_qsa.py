@@ -1,0 +1,219 @@
+"""GPU parity of the index-selected sparse attention path against the fp64 oracle.
+
+Element-by-element comparison on seeded inputs (tolerances: 1e-4 fp32, 2e-2 bf16,
+6e-2 e4m3 max abs), plus the invariants that must hold exactly on the GPU: counts = 1
+returns the V row bit for bit, physical page placement and garbage past counts do not
+change a single output bit, every split-K partition count agrees, and two runs are
+bitwise identical.
+"""
+import copy
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from workloads import device as D
+from gpu_util import TOL, announce, compare, to64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def run_and_ref(case, options=None, rows=None):
+    dc = D.to_device(case, DEV)
+    out = D.run(dc, options=options)
+    torch.cuda.synchronize()
+    ref = oracle.run_case(case, rows=rows)
+    got = out if rows is None else out[torch.as_tensor(rows, device=out.device)]
+    return got, ref, dc
+
+
+def test_c1_tiny_fp32():
+    case = W.c1_tiny_fp32()
+    announce("c1 tiny fp32")
+    got, ref, _ = run_and_ref(case)
+    compare(got, ref, "f32", "c1")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 16])
+def test_c1_split_counts(splits):
+    case = W.c1_tiny_fp32()
+    announce("c1 splits=%d" % splits)
+    got, ref, _ = run_and_ref(case, options={"num_splits": splits})
+    compare(got, ref, "f32", "c1 splits=%d" % splits)
+
+
+def small_decode(seed=7, batch=6, lo=100, hi=700, W_=512, hkv=8, g=4, d=128, dtype="bf16", ps=128,
+                 out="bf16", layers=4, layer=2, pad=0, sel="min"):
+    rng = np.random.default_rng(seed + 5000)
+    cl = rng.integers(lo, hi, size=batch, endpoint=True)
+    return W.make_qsa(name="decode_small", seed=seed, rows=[1] * batch, cache_lengths=cl, page_size=ps,
+                      num_layers=layers, layer_idx=layer, num_kv_heads=hkv, group=g, head_dim=d,
+                      dtype=dtype, out_dtype=out, selection_width=W_, selection=sel,
+                      scale=1 / np.sqrt(d), page_pad=pad)
+
+
+def test_decode_small_bf16():
+    case = small_decode()
+    announce("decode small bf16")
+    got, ref, _ = run_and_ref(case)
+    compare(got, ref, "bf16", "decode small", rel_rms_max=0.01)
+
+
+@pytest.mark.parametrize("g,d,dtype,out", [(1, 64, "bf16", "f32"), (2, 256, "bf16", "bf16"),
+                                           (4, 64, "f32", "f32"), (2, 128, "e4m3", "bf16"),
+                                           (4, 128, "f32", "bf16"), (1, 128, "e4m3", "f32")])
+def test_shapes(g, d, dtype, out):
+    case = small_decode(seed=17 + g + d, batch=3, lo=40, hi=300, W_=200, hkv=3, g=g, d=d, dtype=dtype,
+                        ps=32, out=out, layers=2, layer=1, pad=48, sel="uniform_counts")
+    if dtype == "e4m3":
+        case.meta["note"] = "values N(0,1) cast to e4m3"
+    announce("shapes g=%d d=%d %s->%s" % (g, d, dtype, out))
+    got, ref, _ = run_and_ref(case)
+    compare(got, ref, dtype if dtype != "f32" or out == "f32" else "bf16",
+            "shapes g=%d d=%d %s" % (g, d, dtype))
+
+
+def test_ragged_prefill_rows_and_empty_sequence():
+    case = W.make_qsa(name="ragged", seed=23, rows=[5, 0, 9, 1], cache_lengths=[37, 12, 0, 300],
+                      page_size=16, num_layers=1, layer_idx=0, num_kv_heads=2, group=4, head_dim=128,
+                      dtype="bf16", out_dtype="bf16", selection_width=70, selection="recent", recent=8,
+                      scale=0.088)
+    announce("ragged prefill rows + empty sequence")
+    got, ref, _ = run_and_ref(case, options={"num_splits": 3})
+    compare(got, ref, "bf16", "ragged")
+
+
+def test_counts_edges_zero_negative_clamped():
+    case = W.c1_tiny_fp32()
+    c = copy.copy(case)
+    c.counts = case.counts.copy()
+    c.token_indices = case.token_indices.copy()
+    c.counts[0] = 0
+    c.counts[1] = -5
+    c.counts[2] = 1000          # clamps to the width
+    c.token_indices[2] = np.sort(np.random.default_rng(1).choice(int(c.positions()[2]) + 1, 16,
+                                                                 replace=False))
+    announce("counts edges")
+    for splits in (1, 4):
+        got, ref, _ = run_and_ref(c, options={"num_splits": splits})
+        assert (to64(got[0]) == 0).all() and (to64(got[1]) == 0).all()
+        compare(got, ref, "f32", "counts edges splits=%d" % splits)
+
+
+def test_out_of_contract_entries_are_skipped():
+    """Entries outside the page table, negative ones, and page ids past the pool are
+    skipped by the kernel's own bounds checks (never dereferenced)."""
+    case = W.c1_tiny_fp32()
+    c = copy.copy(case)
+    c.kv = copy.copy(case.kv)
+    c.token_indices = case.token_indices.copy()
+    c.counts = case.counts.copy()
+    # row 1: append an index past every page-table entry; row 3: a negative index
+    n1, n3 = c.counts[1], c.counts[3]
+    c.token_indices[1, n1] = 16 * 4 + 3
+    c.counts[1] = n1 + 1
+    c.token_indices[3, n3] = -1
+    c.counts[3] = n3 + 1
+    announce("out-of-contract entries")
+    got, _, _ = run_and_ref(case)          # reference: the unmodified selection
+    dc = D.to_device(c, DEV)
+    out = D.run(dc)
+    torch.cuda.synchronize()
+    assert torch.equal(out, got)
+
+
+def test_counts_one_is_exact_v_row():
+    case = small_decode(seed=31, batch=5, lo=50, hi=400, W_=64)
+    c = copy.copy(case)
+    c.counts = np.ones_like(case.counts)
+    announce("counts=1 exact")
+    dc = D.to_device(c, DEV)
+    out = D.run(dc)
+    torch.cuda.synchronize()
+    pv = case.kv.pages_view()
+    G = case.num_q_heads // case.kv.num_kv_heads
+    for r in range(case.total_q):
+        p = int(case.token_indices[r, 0])
+        page = int(case.kv.lookup_table[r, p // case.kv.page_size])
+        v = pv[page, 1, case.layer_idx, p % case.kv.page_size]          # [Hkv, D] bf16
+        exp = v.repeat_interleave(G, dim=0)
+        assert torch.equal(out[r].cpu().view(torch.int16), exp.view(torch.int16)), r
+
+
+def test_page_permutation_and_poison_are_bitwise_invariant():
+    case = small_decode(seed=41, batch=4, lo=200, hi=600, W_=256, sel="uniform_counts")
+    dc = D.to_device(case, DEV)
+    base = D.run(dc, options={"num_splits": 2})
+    torch.cuda.synchronize()
+    # permute physical pages
+    kv = case.kv
+    perm = np.random.default_rng(3).permutation(kv.num_pages)
+    st = kv.storage.view(kv.num_pages, kv.page_elems)
+    new = torch.empty_like(st)
+    new[torch.as_tensor(perm)] = st
+    c2 = copy.copy(case)
+    c2.kv = copy.copy(kv)
+    c2.kv.storage = new.view(-1)
+    c2.kv.lookup_table = perm[kv.lookup_table.astype(np.int64)].astype(np.uint32)
+    announce("page permutation")
+    out2 = D.run(D.to_device(c2, DEV), options={"num_splits": 2})
+    torch.cuda.synchronize()
+    assert torch.equal(base, out2), "page placement changed the output"
+    # poison: entries past counts name real, unselected positions whose K/V become NaN
+    c3 = copy.copy(case)
+    c3.kv = copy.copy(kv)
+    c3.kv.storage = kv.storage.clone()
+    c3.token_indices = case.token_indices.copy()
+    pv3 = c3.kv.pages_view()
+    for r in range(case.total_q):
+        n = case.counts[r]
+        pos = int(case.positions()[r])
+        free = np.setdiff1d(np.arange(pos + 1), case.token_indices[r, :n])
+        if len(free) == 0:
+            continue
+        for p in free:
+            pv3[int(kv.lookup_table[r, p // kv.page_size]), :, case.layer_idx, p % kv.page_size] = float("nan")
+        c3.token_indices[r, n:] = free[np.arange(case.token_indices.shape[1] - n) % len(free)]
+    announce("poison past counts")
+    out3 = D.run(D.to_device(c3, DEV), options={"num_splits": 2})
+    torch.cuda.synchronize()
+    assert torch.equal(base, out3), "entries past counts were read"
+
+
+def test_splits_agree_and_runs_are_deterministic():
+    case = small_decode(seed=51, batch=4, lo=300, hi=900, W_=700, out="f32")
+    dc = D.to_device(case, DEV)
+    ref = oracle.run_case(case)
+    outs = {}
+    for s in (1, 2, 3, 7, 16):
+        announce("splits=%d" % s)
+        a = D.run(dc, options={"num_splits": s})
+        b = D.run(dc, options={"num_splits": s})
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), "two runs differ (splits=%d)" % s
+        compare(a, ref, "bf16", "splits=%d" % s)
+        outs[s] = to64(a)
+    for s in (2, 3, 7, 16):
+        assert np.abs(outs[s] - outs[1]).max() <= 2e-6, "split %d disagrees with one split" % s
+
+
+@pytest.mark.parametrize("waves,unroll", [(1, 4), (2, 2), (4, 8), (8, 4)])
+def test_launch_options(waves, unroll):
+    case = small_decode(seed=61, batch=3, lo=100, hi=500, W_=300)
+    announce("waves=%d unroll=%d" % (waves, unroll))
+    got, ref, _ = run_and_ref(case, options={"waves": waves, "unroll": unroll})
+    compare(got, ref, "bf16", "waves=%d unroll=%d" % (waves, unroll))
+
+
+def test_c2_full_size_all_rows():
+    """The bf16 decode workload at full size (64 rows x 8 kv heads, W 2048) in the launch
+    configuration the benchmark times; the oracle covers every row."""
+    announce("c2 full size: generating")
+    case = W.c2_decode_bf16()
+    announce("c2 full size: running")
+    got, ref, _ = run_and_ref(case)
+    compare(got, ref, "bf16", "c2 full", rel_rms_max=0.01)
