@@ -118,6 +118,9 @@ def main():
     ap.add_argument("--unroll", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after warmup, run one device-to-device copy of this many MiB (a kernel "
+                         "of known traffic for calibrating hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run "
@@ -163,19 +166,33 @@ def main():
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
-    ev = HipEvents(args.steps)
+    if args.copy_probe_mib:
+        src = torch.ones(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy probe: %d bytes read, %d bytes written" % (src.numel(), dst.numel()))
+        del src, dst
     log("timing %d steps" % args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        qsa.set_timing_events(*ev.pairs[k])
         step(k)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    # the gather kernel alone: HIP events the library records around it, over the
+    # same number of steps in a second pass (so the timed pass above carries no
+    # event overhead)
+    log("timing the gather kernel with events (%d steps)" % args.steps)
+    ev = HipEvents(args.steps)
+    for k in range(args.steps):
+        qsa.set_timing_events(*ev.pairs[k])
+        step(k)
+    torch.cuda.synchronize()
     qsa.set_timing_events(None, None)
     kern_ms = [ev.ms(k) for k in range(args.steps)]
     ev.close()
-    ms_step = (t1 - t0) * 1e3 / args.steps
     kern_avg = sum(kern_ms) / len(kern_ms)
 
     # parity of the last timed output on every row (the oracle takes well under a second)

@@ -1,7 +1,9 @@
 // Split-K combine ("Struct_msa_attention_ragged_paged" design notes: decode runs
 // over partitioned KV bands and then merges them in a reduction kernel).
 //
-// Each split s left, for every (row, q head), the log2-domain maximum m_s, the sum
+// Each split s left, for every (row, q head), a log2-domain reference m_s (at least the
+// largest score it saw minus a small slack, or a large negative value if it saw no
+// key), the sum
 // l_s = sum_j 2^(t_j - m_s) and acc_s = sum_j 2^(t_j - m_s) V_j. The exact result is
 //   out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,   M = max_s m_s,
 // and a (row, head) that saw no key anywhere (l = 0 everywhere) is written as zeros.
@@ -22,14 +24,13 @@ __global__ void __launch_bounds__(256) splitk_combine_kernel(GatherParams p)
     if (rh >= RH || threadIdx.x / tpr >= per_block)
         return;
     const int S = p.num_splits;
-    float M = kNegInf;
+    float M = kNoKey;
     for (int s = 0; s < S; ++s)
         M = fmaxf(M, p.ws_ml[((int64_t)s * RH + rh) * 2]);
-    const float ref = M == kNegInf ? 0.f : M;
     float L = 0.f, a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
     for (int s = 0; s < S; ++s) {
         const int64_t srh = (int64_t)s * RH + rh;
-        const float c = __builtin_amdgcn_exp2f(p.ws_ml[srh * 2] - ref);
+        const float c = __builtin_amdgcn_exp2f(p.ws_ml[srh * 2] - M);
         L += c * p.ws_ml[srh * 2 + 1];
         const float4 v = *reinterpret_cast<const float4 *>(p.ws_acc + srh * D + d0);
         a0 += c * v.x;

@@ -1,6 +1,5 @@
 // Device-side building blocks shared by the gather kernels (gfx950, wave64):
-// element decode, wavefront reductions, the key-address generator and the
-// online-softmax state merge.
+// element decode, wavefront reductions, sequence lookup and the key-address pipeline.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -17,10 +16,24 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef const __attribute__((address_space(1))) u32x4 global_u32x4;
 
 constexpr float kNegInf = -__builtin_huge_valf();
+// Running reference of a softmax state that has not seen a key yet: finite, so that
+// 2^(kNoKey - kNoKey) = 1 and 2^(kNoKey - real) = 0 need no special cases.
+constexpr float kNoKey = -1e30f;
+// Two bf16 ones packed in a dword (sums a packed pair with one dot instruction).
+constexpr uint32_t kBf16OnePair = 0x3F803F80u;
 
 // 16-byte load through the global address space (global_load_dwordx4 rather than a
 // flat load: the pointer came out of LDS, so the compiler cannot prove where it points).
 __device__ __forceinline__ u32x4 ldg16(const void *p) { return *(global_u32x4 *)(p); }
+
+// Two floats -> two bf16 (round to nearest even) packed in a dword, low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    uint32_t u;
+    __builtin_memcpy(&u, &v, sizeof u);
+    return u;
+}
 
 // Reinterpret one dword as two bf16. (A memcpy from a scalar copy: bit-casting a
 // vector element directly has been seen to read element 0 regardless of the index.)
@@ -82,31 +95,8 @@ __device__ __forceinline__ float team_sum(float x)
     return x;
 }
 
-// Element offset of (position p, plane 0, kv head 0) in a paged leaf, or -1 when
-// the entry does not address the cache (position outside the page table, or page
-// id past the pool); such entries are skipped, never dereferenced.
-__device__ __forceinline__ int64_t key_elem_offset(const CacheAddr &c, int64_t b, int64_t p)
-{
-    if (p < 0)
-        return -1;
-    int64_t lp, slot;
-    if (c.page_shift >= 0) {
-        lp = p >> c.page_shift;
-        slot = p & (c.page_size - 1);
-    } else {
-        lp = p / c.page_size;
-        slot = p - lp * c.page_size;
-    }
-    if (lp >= c.max_pages)
-        return -1;
-    uint32_t page = c.lut[b * c.max_pages + lp];
-    if ((int64_t)page >= c.num_pages)
-        return -1;
-    return (int64_t)page * c.page_stride + c.layer_off + slot * c.slot_stride;
-}
-
-// Sequence of row r: the b with row_off[b] <= r < row_off[b+1] (binary search;
-// rows of empty sequences are skipped naturally).
+// Sequence of row r: the b with row_off[b] <= r < row_off[b+1] (binary search; a
+// chain of dependent loads, used only for very large batches).
 __device__ __forceinline__ int find_seq(const uint32_t *row_off, int batch, uint32_t r)
 {
     int lo = 0, hi = batch - 1;
@@ -120,46 +110,23 @@ __device__ __forceinline__ int find_seq(const uint32_t *row_off, int batch, uint
     return lo;
 }
 
-// Byte address of the plane-0 row of key j of (row r, sequence b, kv head g), or
-// nullptr when the key is not present (past the list, clipped, unused or outside
-// the cache). `pos` is the row's position, `n` the key-list length.
-template <int eb>
-__device__ __forceinline__ const char *key_address(const GatherParams &p, int b, int64_t r,
-                                                   int64_t pos, int g, int64_t j)
+// Sequence of row r, found by the whole wavefront at once: lane t tests sequence
+// base + t, so up to 64 sequences cost one memory round trip. Rows past the last
+// offset belong to the last sequence.
+__device__ __forceinline__ int find_seq_wave(const uint32_t *row_off, int batch, uint32_t r)
 {
-    int64_t off;
-    if (p.list_kind == KEYS_TOKEN_INDICES) {
-        int64_t tok = p.indices[r * p.width + j];
-        off = key_elem_offset(p.kv, b, tok);
-        if (off < 0)
-            return nullptr;
-        return static_cast<const char *>(p.kv.blocks) + (off + (int64_t)g * p.head_dim) * eb;
+    if (batch > 1024)
+        return find_seq(row_off, batch, r);
+    const int lane = threadIdx.x & 63;
+    for (int base = 0; base < batch; base += 64) {
+        const int t = base + lane;
+        const uint32_t lo = t < batch ? row_off[t] : 0xffffffffu;
+        const uint32_t hi = t < batch ? row_off[t + 1] : 0u;
+        const unsigned long long m = __ballot(lo <= r && r < hi);
+        if (m)
+            return base + __ffsll((long long)m) - 1;
     }
-    if (p.list_kind == KEYS_BLOCKS) {
-        int64_t t = j / p.block_size;
-        int64_t i = j - t * p.block_size;
-        int64_t id = p.indices[((int64_t)g * p.total_q + r) * p.width + t];
-        int64_t tok = id * p.block_size + i;
-        if (id < 0 || tok > pos)
-            return nullptr;
-        off = key_elem_offset(p.kv, b, tok);
-        if (off < 0)
-            return nullptr;
-        return static_cast<const char *>(p.kv.blocks) + (off + (int64_t)g * p.head_dim) * eb;
-    }
-    // KEYS_LATENT: window positions first, then listed compressed entries
-    if (j < p.window) {
-        int64_t tok = pos - p.window + 1 + j;
-        off = key_elem_offset(p.kv, b, tok);
-        if (off < 0)
-            return nullptr;
-        return static_cast<const char *>(p.kv.blocks) + off * eb;
-    }
-    int64_t e = p.indices[r * p.width + (j - p.window)];
-    off = key_elem_offset(p.comp, b, e);
-    if (off < 0)
-        return nullptr;
-    return static_cast<const char *>(p.comp.blocks) + off * eb;
+    return batch - 1;
 }
 
 // Number of keys in the list of row r (before splitting).
@@ -174,15 +141,83 @@ __device__ __forceinline__ int64_t key_list_length(const GatherParams &p, int64_
     return p.window + p.width;
 }
 
-// Scale factors for merging two online-softmax states with maxima m and m2
-// (log2-domain scores, -inf when a state has seen no key): the merged maximum is
-// mnew and the states are weighted by c1 = 2^(m - mnew) and c2 = 2^(m2 - mnew).
-__device__ __forceinline__ void merge_scale(float m, float m2, float &c1, float &c2, float &mnew)
+// ------------------------------------------------------------------ key pipeline
+//
+// Key j of (row r, kv head g) reaches its K/V rows through three dependent reads:
+//   1. its list entry (a position, a block id, or a compressed entry number);
+//   2. the page-table entry of the page holding that position;
+//   3. the K and V rows themselves.
+// The gather loops run these as a pipeline, several batches apart. Every stage issues
+// exactly one load per key whether or not the key is present: a key past the list,
+// clipped, unused or outside the cache reads a harmless dummy location and carries
+// present = false, so that all code paths issue the same loads and the compiler can
+// wait for exactly the oldest batch. Entries at or past counts are never loaded.
+
+// Stage 1: address of key jj's list entry (or a dummy, whose value is not used).
+template <int LIST>
+__device__ __forceinline__ const int32_t *entry_ptr(const GatherParams &p, int64_t r, int g, int64_t jj,
+                                                    bool present)
 {
-    mnew = fmaxf(m, m2);
-    float ref = mnew == kNegInf ? 0.f : mnew;
-    c1 = __builtin_amdgcn_exp2f(m - ref);
-    c2 = __builtin_amdgcn_exp2f(m2 - ref);
+    const int32_t *dummy = reinterpret_cast<const int32_t *>(p.row_off);
+    if (!present)
+        return dummy;
+    if constexpr (LIST == KEYS_TOKEN_INDICES)
+        return p.indices + r * p.width + jj;
+    if constexpr (LIST == KEYS_BLOCKS)
+        return p.indices + ((int64_t)g * p.total_q + r) * p.width + jj / p.block_size;
+    return jj < p.window ? dummy : p.indices + r * p.width + (jj - p.window);
+}
+
+// Stage 2 input: the position the entry names, and which leaf holds it.
+struct KeyPos {
+    int64_t tok;       // position (or compressed entry); meaningful when present
+    bool comp;         // latent: compressed leaf
+    bool present;
+};
+
+template <int LIST>
+__device__ __forceinline__ KeyPos key_pos(const GatherParams &p, int64_t pos, int64_t jj, int32_t raw,
+                                          bool present)
+{
+    KeyPos k{raw, false, present};
+    if constexpr (LIST == KEYS_BLOCKS) {
+        const int64_t t = jj / p.block_size;
+        k.tok = (int64_t)raw * p.block_size + (jj - t * p.block_size);
+        k.present = present && raw >= 0 && k.tok <= pos;
+    } else if constexpr (LIST == KEYS_LATENT) {
+        const bool win = jj < p.window;
+        k.tok = win ? pos - p.window + 1 + jj : raw;
+        k.comp = !win;
+    }
+    k.present = k.present && k.tok >= 0;
+    return k;
+}
+
+// Stage 2: address of the page-table entry of k (or a dummy). Updates k.present for
+// positions beyond the page table.
+__device__ __forceinline__ const uint32_t *page_entry_ptr(const GatherParams &p, int b, KeyPos &k,
+                                                          int32_t &slot)
+{
+    const CacheAddr &c = k.comp ? p.comp : p.kv;
+    // positions are below 2^31 (int32 lists); larger ones are outside every page table
+    k.present = k.present && k.tok < (int64_t(1) << 31);
+    const uint64_t t = (uint64_t)(k.tok & 0x7fffffff);
+    const int64_t lp = (int64_t)((t * c.magic) >> c.magic_shift);
+    slot = (int32_t)(t - (uint64_t)lp * (uint64_t)c.page_size);
+    k.present = k.present && lp < c.max_pages;
+    return k.present ? c.lut + (int64_t)b * c.max_pages + lp : c.lut;
+}
+
+// Stage 3: byte address of k's plane-0 row for kv head g (or `dummy`).
+template <int EB, int LIST>
+__device__ __forceinline__ const char *row_address(const GatherParams &p, const KeyPos &k, uint32_t page,
+                                                   int32_t slot, int g, const char *dummy, bool &present)
+{
+    const CacheAddr &c = k.comp ? p.comp : p.kv;
+    present = k.present && (int64_t)page < c.num_pages;
+    const int64_t head = LIST == KEYS_LATENT ? 0 : (int64_t)g * p.head_dim;
+    const int64_t off = (int64_t)page * c.page_stride + c.layer_off + (int64_t)slot * c.slot_stride + head;
+    return present ? static_cast<const char *>(c.blocks) + off * EB : dummy;
 }
 
 __device__ __forceinline__ void store_out(void *out, int32_t out_dtype, int64_t idx, float v)

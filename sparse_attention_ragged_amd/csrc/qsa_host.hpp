@@ -27,7 +27,8 @@ struct CacheAddr {
     int64_t max_pages;
     int64_t num_pages;
     int32_t page_size;
-    int32_t page_shift;     // log2(page_size) when a power of two, else -1
+    int32_t magic_shift;    // position -> logical page: (pos * magic) >> magic_shift, exact for pos < 2^31
+    uint64_t magic;
 };
 
 // Key-list kinds the gather kernels walk for one (row, kv head).

@@ -11,9 +11,10 @@ namespace qsa {
 namespace {
 thread_local std::string g_error;
 
-// Workgroups a launch should provide to keep all 256 compute units of an MI355X
-// busy with several resident workgroups each (8 XCDs x 32 CUs).
-constexpr int64_t kTargetWorkgroups = 256 * 8;
+// Workgroups a launch should provide: two per compute unit of an MI355X (8 XCDs x
+// 32 CUs) keeps every CU streaming; more, shorter workgroups only add prologue and
+// split-K combine cost.
+constexpr int64_t kTargetWorkgroups = 256 * 2;
 // A split shorter than this many keys spends more on its prologue/epilogue than on
 // gathering.
 constexpr int64_t kMinKeysPerSplit = 128;
@@ -123,10 +124,10 @@ qsa_status plan_gather(const qsa_ragged_q *q, int64_t num_kv_heads, int32_t dtyp
         o = *opts;
     if (o.num_splits < 0 || o.num_splits > kMaxSplits)
         return fail(QSA_ERR_UNSUPPORTED, "num_splits must be in [0, %d]", kMaxSplits);
-    if (o.waves < 0 || o.waves > 8 || (o.waves & (o.waves - 1)))
-        return fail(QSA_ERR_UNSUPPORTED, "waves must be 0 (automatic) or 1, 2, 4, 8");
-    if (!(o.unroll == 0 || o.unroll == 2 || o.unroll == 4 || o.unroll == 8))
-        return fail(QSA_ERR_UNSUPPORTED, "unroll must be 0 (automatic), 2, 4 or 8");
+    if (o.waves < 0 || o.waves > 8)
+        return fail(QSA_ERR_UNSUPPORTED, "waves must be in [0, 8] (0 = automatic)");
+    if (o.unroll < 0 || o.unroll > 8)
+        return fail(QSA_ERR_UNSUPPORTED, "unroll must be in [0, 8]");
     plan->waves = o.waves ? o.waves : 4;
     plan->unroll = o.unroll ? o.unroll : 4;
     plan->key_capacity = key_capacity;
@@ -176,10 +177,15 @@ CacheAddr cache_addr(const qsa_paged_cache *c, uint32_t layer)
     a.max_pages = c->max_pages;
     a.num_pages = c->num_pages;
     a.page_size = (int32_t)c->page_size;
-    a.page_shift = -1;
-    for (int s = 0; s < 31; ++s)
-        if ((int64_t(1) << s) == c->page_size)
-            a.page_shift = s;
+    // Division by the page size as a multiply-high: with k = ceil(log2(page_size)) and
+    // magic = ceil(2^(31+k) / page_size), (pos * magic) >> (31+k) == pos / page_size
+    // for every 0 <= pos < 2^31 (the rounding error stays below 2^-k <= 1/page_size).
+    int k = 0;
+    while ((int64_t(1) << k) < c->page_size)
+        ++k;
+    const unsigned __int128 num = (unsigned __int128)1 << (31 + k);
+    a.magic = (uint64_t)((num + (unsigned __int128)c->page_size - 1) / (unsigned __int128)c->page_size);
+    a.magic_shift = 31 + k;
     return a;
 }
 

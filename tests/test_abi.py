@@ -116,7 +116,7 @@ def test_workspace_checks(qsa):
     assert n.value == 0
 
 
-@pytest.mark.parametrize("opts", [(65, 0, 0, 0), (0, 3, 0, 0), (0, 16, 0, 0), (0, 0, 3, 0), (-1, 0, 0, 0)])
+@pytest.mark.parametrize("opts", [(65, 0, 0, 0), (0, 9, 0, 0), (0, 16, 0, 0), (0, 0, 9, 0), (-1, 0, 0, 0)])
 def test_bad_launch_options(qsa, opts):
     assert call_qsa(qsa, opts=qsa.LaunchOptions(*opts)) == 4, msg(qsa)
 
