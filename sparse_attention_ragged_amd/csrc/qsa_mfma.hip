@@ -1,10 +1,389 @@
-// Gather-attention on matrix cores (groups of 8 or more query heads per kv head).
+// Gather-attention on matrix cores (groups of 8 or 16 query heads per kv head).
+//
+// One workgroup owns one (query row, kv head, split); each wavefront of it walks its
+// own tiles of 32 keys of the split (the workgroup merges the wavefronts at the end).
+// Per tile, with gfx950 16x16x32 MFMAs (lane l: i = l % 16, q = l / 16):
+//
+//  * S^T = K . Q^T   A = 16 keys x 32 dims of K, straight from global memory (lane
+//                    holds 8 consecutive dims of key i), B = Q^T (8 dims of head i,
+//                    loaded once). Two key halves x head_dim/32 chunks of MFMAs; C
+//                    holds, per lane, keys 4q..4q+3 (+16) of head i.
+//  * softmax         per head i, over the four lanes sharing i, in the log2 domain
+//                    with the same lazy rescale as the wavefront kernel.
+//  * O^T += V^T P^T  B = P^T comes straight out of the S^T accumulator layout (the
+//                    MFMA's key order is chosen to match it); A = V^T is read from an
+//                    LDS copy of the V tile with the transposing 64-bit LDS load, one
+//                    read per 4 keys x 16 dims.
+//
+// fp8 e4m3 ("Struct_msa_attention_ragged_paged": scale-free FP8, FP32 accumulation):
+// S^T uses the fp8 MFMA on the raw codes; V is widened to bf16 (exactly) on its way
+// into LDS, so P stays bf16 in P.V. Groups below 16 pad the head dimension of the
+// MFMA with zero query rows whose results are dropped.
+//
+// Keys reach their rows through the same three-stage address pipeline as the
+// wavefront kernel (list entry -> page-table entry -> rows), issued a tile ahead.
+#include <type_traits>
+
 #include "qsa_device.hpp"
 
 namespace qsa {
 
-bool mfma_supported(int32_t, int32_t, int32_t) { return false; }
+namespace {
 
-int launch_gather_mfma(const GatherParams &, void *) { return (int)hipErrorInvalidValue; }
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(1))) u32x2 global_u32x2;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+
+constexpr int kMfmaMaxWaves = 4;
+constexpr int kTileKeys = 32;
+constexpr float kSlack = 8.0f;
+
+__device__ __forceinline__ u32x2 ldg8(const void *p) { return *(global_u32x2 *)(p); }
+
+__device__ __forceinline__ long as_long(u32x2 v)
+{
+    long r;
+    __builtin_memcpy(&r, &v, sizeof r);
+    return r;
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v)
+{
+    bf16x8_t r;
+    __builtin_memcpy(&r, &v, sizeof r);
+    return r;
+}
+
+// 8 e4m3 codes -> 8 bf16 (exact: every e4m3 value is a bf16 value)
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 w)
+{
+    float f[8];
+    e4m3x4_to_f32(w[0], f);
+    e4m3x4_to_f32(w[1], f + 4);
+    return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                 pack_bf16x2(f[6], f[7])};
+}
+
+template <int DT, int D, int LIST>
+__global__ void __launch_bounds__(64 * kMfmaMaxWaves) gather_mfma_kernel(GatherParams p)
+{
+    constexpr int EB = Elem<DT>::bytes;
+    constexpr int NC = D / 32;                  // 32-dim chunks of QK^T
+    constexpr int NDT = D / 16;                 // 16-dim tiles of the output
+    constexpr int VROW = D + 8;                 // LDS row of the V tile, in bf16 (+16 B)
+    constexpr int kVBytes = kMfmaMaxWaves * kTileKeys * VROW * 2;
+    constexpr int kMergeBytes = kMfmaMaxWaves * 16 * (D + 2) * 4;
+    constexpr int kSmem = kVBytes > kMergeBytes ? kVBytes : kMergeBytes;
+    static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
+    using Chunk = typename std::conditional<DT == QSA_BF16, u32x4, u32x2>::type;
+    __shared__ __attribute__((aligned(16))) char smem[kSmem];
+
+    const int S = p.num_splits;
+    const int Hkv = p.num_kv_heads;
+    const int G = p.group;
+    int64_t bid = blockIdx.x;
+    const int g = (int)(bid % Hkv);
+    bid /= Hkv;
+    const int s = (int)(bid % S);
+    const int64_t r = bid / S;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int NW = blockDim.x >> 6;
+    const int li = lane & 15;
+    const int lq = lane >> 4;
+    uint16_t *s_v = reinterpret_cast<uint16_t *>(smem) + wave * kTileKeys * VROW;
+
+    // prologue: list length, sequence and the q fragments go out together
+    const int64_t n = key_list_length(p, r);
+    const char *qrow0 = static_cast<const char *>(p.q) + ((r * p.num_q_heads + (int64_t)g * G) * D) * EB;
+    const bool head_real = li < G;
+    const char *qrow = head_real ? qrow0 + (int64_t)li * D * EB : qrow0;
+    Chunk qf[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        if constexpr (DT == QSA_BF16) {
+            const u32x4 v = ldg16(qrow + (32 * c + 8 * lq) * EB);
+            qf[c] = head_real ? v : u32x4{0, 0, 0, 0};
+        } else {
+            const u32x2 v = ldg8(qrow + (32 * c + 8 * lq) * EB);
+            qf[c] = head_real ? v : u32x2{0, 0};
+        }
+    }
+    const int b = find_seq_wave(p.row_off, p.batch, (uint32_t)r);
+    int64_t pos = 0;
+    if constexpr (LIST != KEYS_TOKEN_INDICES)
+        pos = (int64_t)p.cache_lengths[b] + (r - (int64_t)p.row_off[b]);
+    const int64_t j0 = (int64_t)s * p.split_keys;
+    const int64_t j1 = n < j0 + p.split_keys ? n : j0 + p.split_keys;
+    const int64_t per_batch = (int64_t)NW * kTileKeys;
+    const int nb = j1 > j0 ? (int)((j1 - j0 + per_batch - 1) / per_batch) : 0;
+    const int64_t vdelta = LIST == KEYS_LATENT ? 0 : p.kv.plane_stride * EB;
+    const char *dummy = qrow0;                   // a readable row for absent keys
+
+    float m = kNoKey, lsum = 0.f;                // head li (shared by the 4 lanes of li)
+    f32x4_t acc[NDT];
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+        acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    struct Entries { int32_t raw[2]; };
+    struct Pages { KeyPos k[2]; int32_t slot[2]; uint32_t page[2]; };
+    struct Rows { Chunk k[2][NC], v[2][NC]; bool ok[2]; };
+
+    // this lane's two keys of tile `batch`: 16*h + li, h = 0, 1
+    auto key_index = [&](int batch, int h) -> int64_t {
+        return j0 + (int64_t)batch * per_batch + (int64_t)wave * kTileKeys + 16 * h + li;
+    };
+    auto load_entries = [&](int batch, Entries &E) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t jj = key_index(batch, h);
+            E.raw[h] = *entry_ptr<LIST>(p, r, g, jj, jj < j1);
+        }
+    };
+    auto load_pages = [&](int batch, const Entries &E, Pages &P) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t jj = key_index(batch, h);
+            P.k[h] = key_pos<LIST>(p, pos, jj, E.raw[h], jj < j1);
+            P.page[h] = *page_entry_ptr(p, b, P.k[h], P.slot[h]);
+        }
+    };
+    auto load_rows = [&](const Pages &P, Rows &R) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            bool ok;
+            const char *a = row_address<EB, LIST>(p, P.k[h], P.page[h], P.slot[h], g, dummy, ok);
+            R.ok[h] = ok;
+            const char *ka = ok ? a : dummy;
+            const char *va = ok ? a + vdelta : dummy;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                if constexpr (DT == QSA_BF16) {
+                    R.k[h][c] = ldg16(ka + (32 * c + 8 * lq) * EB);
+                    R.v[h][c] = ldg16(va + (32 * c + 8 * lq) * EB);
+                } else {
+                    R.k[h][c] = ldg8(ka + (32 * c + 8 * lq) * EB);
+                    R.v[h][c] = ldg8(va + (32 * c + 8 * lq) * EB);
+                }
+            }
+        }
+    };
+    auto consume = [&](const Rows &R) {
+        // key-presence mask of the tile: bit k = key 16*h + k%16 present
+        const uint32_t m0 = (uint32_t)(__ballot(R.ok[0]) & 0xffffu);
+        const uint32_t m1 = (uint32_t)(__ballot(R.ok[1]) & 0xffffu);
+        const uint32_t present = m0 | (m1 << 16);
+        // S^T (two 16-key halves)
+        f32x4_t st[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            st[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                if constexpr (DT == QSA_BF16)
+                    st[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k[h][c]), as_bf16x8(qf[c]),
+                                                                    st[h], 0, 0, 0);
+                else
+                    st[h] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(R.k[h][c]), as_long(qf[c]), st[h],
+                                                                          0, 0, 0);
+            }
+        }
+        // V tile -> LDS (bf16 rows); read back transposed below by this wavefront only.
+        // LDS operations of one wavefront execute in order; the empty asm statements
+        // keep the compiler from moving the accesses across each other.
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                u32x4 v;
+                if constexpr (DT == QSA_BF16)
+                    v = R.v[h][c];
+                else
+                    v = e4m3x8_to_bf16x8(R.v[h][c]);
+                *reinterpret_cast<u32x4 *>(s_v + (16 * h + li) * VROW + 32 * c + 8 * lq) = v;
+            }
+        asm volatile("" ::: "memory");
+        // scores in the log2 domain, absent keys at -inf
+        float sc[2][4];
+        float mx = m;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = 16 * h + 4 * lq + i;
+                const float v = st[h][i] * p.scale_log2;
+                sc[h][i] = (present >> key) & 1u ? v : kNegInf;
+                mx = fmaxf(mx, sc[h][i]);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (__any(mx > m + kSlack)) {
+            const float alpha = __builtin_amdgcn_exp2f(m - mx);
+            lsum *= alpha;
+#pragma unroll
+            for (int t = 0; t < NDT; ++t)
+                acc[t] *= alpha;
+            m = mx;
+        }
+        float w[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                w[h][i] = __builtin_amdgcn_exp2f(sc[h][i] - m);
+                lsum += w[h][i];
+            }
+        // P^T as the B operand: k-slot t < 4 is key 4q + t, t >= 4 is key 16 + 4q + t - 4
+        const u32x4 pb = {pack_bf16x2(w[0][0], w[0][1]), pack_bf16x2(w[0][2], w[0][3]),
+                          pack_bf16x2(w[1][0], w[1][1]), pack_bf16x2(w[1][2], w[1][3])};
+        // V^T as the A operand via transposing LDS reads: source lane (q, 4j + e4) reads
+        // 4 dims of key kb + j, and lane (q, i) receives dim i of keys kb .. kb + 3
+        const int jr = li >> 2, qd = li & 3;
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) {
+            const int col = 16 * t + 4 * qd;
+            const s16x4_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4 *)(s_v + (4 * lq + jr) * VROW + col));
+            const s16x4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4 *)(s_v + (16 + 4 * lq + jr) * VROW + col));
+            u32x4 av;
+            __builtin_memcpy(&av, &a0, 8);
+            __builtin_memcpy(reinterpret_cast<char *>(&av) + 8, &a1, 8);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(pb), acc[t], 0, 0, 0);
+        }
+    };
+
+    if (nb > 0) {
+        Entries E0, E1;
+        Pages P0, P1;
+        Rows R0, R1;
+        load_entries(0, E0);
+        load_entries(1, E1);
+        load_pages(0, E0, P0);
+        load_entries(2, E0);
+        load_pages(1, E1, P1);
+        load_rows(P0, R0);
+        load_entries(3, E1);
+        load_pages(2, E0, P0);
+        load_rows(P1, R1);
+        consume(R0);
+        for (int i = 2; i <= nb; i += 2) {
+            load_entries(i + 2, E0);
+            load_pages(i + 1, E1, P1);
+            load_rows(P0, R0);
+            consume(R1);
+            if (i + 1 > nb)
+                break;
+            load_entries(i + 3, E1);
+            load_pages(i + 2, E0, P0);
+            load_rows(P1, R1);
+            consume(R0);
+        }
+    }
+
+    // per-head state of this wavefront: sum the four lanes of each head
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+
+    // merge the wavefronts through LDS: s_ml [NW][16][2], s_acc [NW][16][D]
+    __syncthreads();
+    float *s_ml = reinterpret_cast<float *>(smem);
+    float *s_acc = s_ml + kMfmaMaxWaves * 16 * 2;
+    if (lq == 0) {
+        s_ml[(wave * 16 + li) * 2] = m;
+        s_ml[(wave * 16 + li) * 2 + 1] = lsum;
+    }
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            s_acc[(wave * 16 + li) * D + 16 * t + 4 * lq + i] = acc[t][i];
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += blockDim.x) {
+        const int h = idx / D;
+        const int d = idx - h * D;
+        float M = kNoKey;
+        for (int w = 0; w < NW; ++w)
+            M = fmaxf(M, s_ml[(w * 16 + h) * 2]);
+        float L = 0.f, A = 0.f;
+        for (int w = 0; w < NW; ++w) {
+            const float c = __builtin_amdgcn_exp2f(s_ml[(w * 16 + h) * 2] - M);
+            L += c * s_ml[(w * 16 + h) * 2 + 1];
+            A += c * s_acc[(w * 16 + h) * D + d];
+        }
+        const int64_t rh = r * p.num_q_heads + (int64_t)g * G + h;
+        if (S == 1) {
+            store_out(p.out, p.out_dtype, rh * D + d, L > 0.f ? A / L : 0.f);
+        } else {
+            const int64_t srh = (int64_t)s * p.total_q * p.num_q_heads + rh;
+            p.ws_acc[srh * D + d] = A;
+            if (d == 0) {
+                p.ws_ml[srh * 2] = M;
+                p.ws_ml[srh * 2 + 1] = L;
+            }
+        }
+    }
+}
+
+template <int DT, int D, int LIST>
+int launch_mfma(const GatherParams &p, void *stream)
+{
+    const int64_t grid = p.total_q * (int64_t)p.num_kv_heads * p.num_splits;
+    if (grid <= 0)
+        return 0;
+    if (grid > 0x7fffffff)
+        return (int)hipErrorInvalidConfiguration;
+    const int waves = p.waves < kMfmaMaxWaves ? p.waves : kMfmaMaxWaves;
+    hipLaunchKernelGGL((gather_mfma_kernel<DT, D, LIST>), dim3((unsigned)grid), dim3(64 * waves), 0,
+                       static_cast<hipStream_t>(stream), p);
+    return (int)hipGetLastError();
+}
+
+template <int LIST>
+int launch_mfma_t(const GatherParams &p, void *stream)
+{
+    if (p.dtype == QSA_BF16) {
+        switch (p.head_dim) {
+        case 64: return launch_mfma<QSA_BF16, 64, LIST>(p, stream);
+        case 128: return launch_mfma<QSA_BF16, 128, LIST>(p, stream);
+        case 256: return launch_mfma<QSA_BF16, 256, LIST>(p, stream);
+        default: return (int)hipErrorInvalidValue;
+        }
+    }
+    if (p.dtype == QSA_FP8_E4M3) {
+        switch (p.head_dim) {
+        case 64: return launch_mfma<QSA_FP8_E4M3, 64, LIST>(p, stream);
+        case 128: return launch_mfma<QSA_FP8_E4M3, 128, LIST>(p, stream);
+        case 256: return launch_mfma<QSA_FP8_E4M3, 256, LIST>(p, stream);
+        default: return (int)hipErrorInvalidValue;
+        }
+    }
+    return (int)hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool mfma_supported(int32_t dtype, int32_t group, int32_t head_dim)
+{
+    return (dtype == QSA_BF16 || dtype == QSA_FP8_E4M3) && group >= 8 && group <= 16 &&
+           (head_dim == 64 || head_dim == 128 || head_dim == 256);
+}
+
+int launch_gather_mfma(const GatherParams &p, void *stream)
+{
+    switch (p.list_kind) {
+    case KEYS_TOKEN_INDICES: return launch_mfma_t<KEYS_TOKEN_INDICES>(p, stream);
+    case KEYS_BLOCKS: return launch_mfma_t<KEYS_BLOCKS>(p, stream);
+    case KEYS_LATENT: return launch_mfma_t<KEYS_LATENT>(p, stream);
+    default: return (int)hipErrorInvalidValue;
+    }
+}
 
 }  // namespace qsa

@@ -274,7 +274,7 @@ def make_qsa(*, name="qsa", seed, rows, cache_lengths, page_size, num_layers, la
                 sel = np.sort(rng.choice(pos + 1, n, replace=False))
             elif selection == "recent":
                 n = min(W, pos + 1)
-                nr = min(recent, pos + 1)
+                nr = min(recent, n)
                 tail = np.arange(pos + 1 - nr, pos + 1)
                 early = rng.choice(pos + 1 - nr, n - nr, replace=False) if n > nr else np.zeros(0, np.int64)
                 sel = np.sort(np.concatenate([early, tail]))
