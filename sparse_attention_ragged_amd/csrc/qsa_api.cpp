@@ -52,7 +52,9 @@ qsa_status run(const GatherParams &p, const Plan &plan, void *stream)
     if (t_ev_start && t_ev_stop)
         err = record_event(t_ev_start, stream);
     if (!err)
-        err = plan.mfma ? launch_gather_mfma(p, stream) : launch_gather_valu(p, stream);
+        err = plan.path == PATH_MFMA_WIDE ? launch_gather_mfma_wide(p, stream)
+              : plan.path == PATH_MFMA  ? launch_gather_mfma(p, stream)
+                                        : launch_gather_valu(p, stream);
     if (!err && t_ev_start && t_ev_stop)
         err = record_event(t_ev_stop, stream);
     if (!err && plan.num_splits > 1)
@@ -90,7 +92,7 @@ qsa_status sparse_plan(const qsa_ragged_q *q, const qsa_paged_cache *kv, int64_t
     if (s == QSA_OK && W < 0)
         s = fail(QSA_ERR_SHAPE, "selection_width must be >= 0");
     if (s == QSA_OK)
-        s = plan_gather(q, kv->num_kv_heads, q->dtype, W, 1, opts, plan);
+        s = plan_gather(q, kv->num_kv_heads, q->dtype, KEYS_TOKEN_INDICES, W, 1, opts, plan);
     return s;
 }
 
@@ -110,7 +112,7 @@ qsa_status block_plan(const qsa_ragged_q *q, const qsa_paged_cache *kv, int64_t 
     if (s == QSA_OK && topk * block_size > (int64_t(1) << 30))
         s = fail(QSA_ERR_SHAPE, "topk * block_size out of range");
     if (s == QSA_OK)
-        s = plan_gather(q, kv->num_kv_heads, q->dtype, topk * block_size, block_size, opts, plan);
+        s = plan_gather(q, kv->num_kv_heads, q->dtype, KEYS_BLOCKS, topk * block_size, block_size, opts, plan);
     return s;
 }
 
@@ -125,7 +127,7 @@ qsa_status latent_plan(const qsa_ragged_q *q, int64_t window, int64_t num_comp,
         return fail(QSA_ERR_SHAPE, "num_comp must be >= 0");
     if (window + num_comp > (int64_t(1) << 30))
         return fail(QSA_ERR_SHAPE, "window + num_comp out of range");
-    return plan_gather(q, 1, q->dtype, window + num_comp, 1, opts, plan);
+    return plan_gather(q, 1, q->dtype, KEYS_LATENT, window + num_comp, 1, opts, plan);
 }
 
 }  // namespace

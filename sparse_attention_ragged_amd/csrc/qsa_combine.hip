@@ -7,6 +7,7 @@
 // l_s = sum_j 2^(t_j - m_s) and acc_s = sum_j 2^(t_j - m_s) V_j. The exact result is
 //   out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,   M = max_s m_s,
 // and a (row, head) that saw no key anywhere (l = 0 everywhere) is written as zeros.
+// A per-head sink logit (latent attention) joins the denominator here, once.
 #include "qsa_device.hpp"
 
 namespace qsa {
@@ -38,12 +39,12 @@ __global__ void __launch_bounds__(256) splitk_combine_kernel(GatherParams p)
         a2 += c * v.z;
         a3 += c * v.w;
     }
-    const bool any = L > 0.f;
+    const float f = final_factor(p, rh % p.num_q_heads, M, L);
     const int64_t o = rh * D + d0;
-    store_out(p.out, p.out_dtype, o + 0, any ? a0 / L : 0.f);
-    store_out(p.out, p.out_dtype, o + 1, any ? a1 / L : 0.f);
-    store_out(p.out, p.out_dtype, o + 2, any ? a2 / L : 0.f);
-    store_out(p.out, p.out_dtype, o + 3, any ? a3 / L : 0.f);
+    store_out(p.out, p.out_dtype, o + 0, a0 * f);
+    store_out(p.out, p.out_dtype, o + 1, a1 * f);
+    store_out(p.out, p.out_dtype, o + 2, a2 * f);
+    store_out(p.out, p.out_dtype, o + 3, a3 * f);
 }
 
 }  // namespace

@@ -220,6 +220,21 @@ __device__ __forceinline__ const char *row_address(const GatherParams &p, const 
     return present ? static_cast<const char *>(c.blocks) + off * EB : dummy;
 }
 
+// Normalising factor of a finished softmax state (reference M, sum L, log2 domain):
+// out = acc * factor. With a sink logit (natural-log units, not scaled) the sink
+// joins the denominator once; a row with no keys is all zeros.
+__device__ __forceinline__ float final_factor(const GatherParams &p, int64_t head, float M, float L)
+{
+    float c = 1.f;
+    if (p.sink) {
+        const float sl = p.sink[head] * 1.44269504088896340736f;
+        const float M2 = fmaxf(M, sl);
+        c = __builtin_amdgcn_exp2f(M - M2);
+        L = L * c + __builtin_amdgcn_exp2f(sl - M2);
+    }
+    return L > 0.f ? c / L : 0.f;
+}
+
 __device__ __forceinline__ void store_out(void *out, int32_t out_dtype, int64_t idx, float v)
 {
     if (out_dtype == QSA_BF16)

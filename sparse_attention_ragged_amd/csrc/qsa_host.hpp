@@ -70,8 +70,14 @@ struct GatherParams {
     float *ws_ml;                    // [S, total_q, Hq, 2]
 };
 
+enum GatherPath : int32_t {
+    PATH_VALU = 0,        // groups of 1, 2, 4: wavefront dot products
+    PATH_MFMA = 1,        // groups of 8..16: matrix cores, wavefronts split the keys
+    PATH_MFMA_WIDE = 2,   // latent groups of 17..64: matrix cores, wavefronts split the heads
+};
+
 struct Plan {
-    bool mfma;
+    int32_t path;
     int32_t num_splits;
     int32_t waves;
     int32_t unroll;
@@ -84,7 +90,7 @@ struct Plan {
 // Validation + planning (qsa_plan.cpp). They never touch the device.
 qsa_status check_cache(const qsa_paged_cache *c, const char *what, int64_t planes);
 qsa_status check_q(const qsa_ragged_q *q, const qsa_paged_cache *c, bool same_heads_as_cache);
-qsa_status plan_gather(const qsa_ragged_q *q, int64_t num_kv_heads, int32_t dtype,
+qsa_status plan_gather(const qsa_ragged_q *q, int64_t num_kv_heads, int32_t dtype, int32_t list_kind,
                        int64_t key_capacity, int64_t split_unit, const qsa_launch_options *opts,
                        Plan *plan);
 CacheAddr cache_addr(const qsa_paged_cache *c, uint32_t layer);
@@ -92,6 +98,7 @@ CacheAddr cache_addr(const qsa_paged_cache *c, uint32_t layer);
 // Launchers (qsa_*.hip). Return a hipError_t value (0 = success).
 int launch_gather_valu(const GatherParams &p, void *stream);
 int launch_gather_mfma(const GatherParams &p, void *stream);
+int launch_gather_mfma_wide(const GatherParams &p, void *stream);
 int launch_splitk_combine(const GatherParams &p, void *stream);
 int record_event(void *event, void *stream);
 const char *hip_error_text(int err);
@@ -99,5 +106,6 @@ const char *hip_error_text(int err);
 // Which (dtype, group, head_dim) combinations have a built kernel.
 bool valu_supported(int32_t dtype, int32_t group, int32_t head_dim);
 bool mfma_supported(int32_t dtype, int32_t group, int32_t head_dim);
+bool mfma_wide_supported(int32_t dtype, int32_t group, int32_t head_dim, int32_t list_kind);
 
 }  // namespace qsa

@@ -320,7 +320,7 @@ __global__ void __launch_bounds__(64 * kMfmaMaxWaves) gather_mfma_kernel(GatherP
         }
         const int64_t rh = r * p.num_q_heads + (int64_t)g * G + h;
         if (S == 1) {
-            store_out(p.out, p.out_dtype, rh * D + d, L > 0.f ? A / L : 0.f);
+            store_out(p.out, p.out_dtype, rh * D + d, A * final_factor(p, (int64_t)g * G + h, M, L));
         } else {
             const int64_t srh = (int64_t)s * p.total_q * p.num_q_heads + rh;
             p.ws_acc[srh * D + d] = A;

@@ -107,14 +107,23 @@ qsa_status check_q(const qsa_ragged_q *q, const qsa_paged_cache *c, bool same_he
 // With more than one split every workgroup writes an (m, l, acc) partial to the
 // workspace and a combine kernel merges them; with one split the gather kernel
 // writes the output itself.
-qsa_status plan_gather(const qsa_ragged_q *q, int64_t num_kv_heads, int32_t dtype,
+qsa_status plan_gather(const qsa_ragged_q *q, int64_t num_kv_heads, int32_t dtype, int32_t list_kind,
                        int64_t key_capacity, int64_t split_unit, const qsa_launch_options *opts,
                        Plan *plan)
 {
     const int64_t group = q->num_q_heads / num_kv_heads;
-    plan->mfma = group >= 8;
-    const bool built = plan->mfma ? mfma_supported(dtype, (int32_t)group, (int32_t)q->head_dim)
-                                  : valu_supported(dtype, (int32_t)group, (int32_t)q->head_dim);
+    const int32_t G = (int32_t)group, Dh = (int32_t)q->head_dim;
+    bool built;
+    if (group > 16) {
+        plan->path = PATH_MFMA_WIDE;
+        built = group <= 64 && mfma_wide_supported(dtype, G, Dh, list_kind);
+    } else if (group >= 8) {
+        plan->path = PATH_MFMA;
+        built = mfma_supported(dtype, G, Dh);
+    } else {
+        plan->path = PATH_VALU;
+        built = valu_supported(dtype, G, Dh);
+    }
     if (!built)
         return fail(QSA_ERR_UNSUPPORTED,
                     "no kernel built for dtype %d, group %lld, head_dim %lld", dtype,

@@ -1,0 +1,88 @@
+"""GPU parity of latent window + compressed + sink attention against the fp64 oracle,
+over every kernel family it can run on (wavefront dot products for 1-4 heads, the
+key-split matrix-core kernel for 8-16 heads, the head-split matrix-core kernel for
+17-64 heads), plus the full-size latent workload on sampled rows."""
+import copy
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from workloads import device as D
+from gpu_util import announce, compare, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def latent_small(seed=31, heads=64, d=512, dtype="bf16", out="bf16", unused=0.1, num_comp=40, window=24,
+                 dec=(300, 1000, 77), pre=(500,), pre_rows=9):
+    return W.make_latent(name="lat_small", seed=seed, decode_positions=list(dec), prefill_positions=list(pre),
+                         prefill_rows=pre_rows, num_heads=heads, head_dim=d, dtype=dtype, out_dtype=out,
+                         window=window, swa_page_size=16, comp_page_size=32, num_comp=num_comp, comp_ratio=4,
+                         unused_frac=unused, scale=1 / np.sqrt(d))
+
+
+def run(case, options=None, rows=None):
+    dc = D.to_device(case, DEV)
+    out = D.run(dc, options=options)
+    torch.cuda.synchronize()
+    ref = oracle.run_case(case, rows=rows)
+    got = out if rows is None else out[torch.as_tensor(rows, device=out.device)]
+    return got, ref
+
+
+@pytest.mark.parametrize("heads,d,out", [(64, 512, "bf16"), (64, 512, "f32"), (32, 256, "f32"), (48, 128, "f32"),
+                                         (16, 128, "f32"), (8, 256, "bf16"), (4, 128, "f32"), (2, 64, "f32")])
+def test_latent_shapes(heads, d, out):
+    case = latent_small(heads=heads, d=d, out=out)
+    announce("latent heads=%d d=%d out=%s" % (heads, d, out))
+    got, ref = run(case)
+    compare(got, ref, "bf16", "latent h=%d d=%d" % (heads, d), rel_rms_max=0.01)
+
+
+@pytest.mark.parametrize("heads", [64, 16, 4])
+@pytest.mark.parametrize("splits", [2, 5])
+def test_latent_splits_apply_sink_once(heads, splits):
+    case = latent_small(seed=33, heads=heads, d=128, out="f32", num_comp=60)
+    announce("latent splits=%d heads=%d" % (splits, heads))
+    got, ref = run(case, options={"num_splits": splits})
+    compare(got, ref, "bf16", "latent splits=%d" % splits)
+
+
+def test_latent_window_only_and_no_sink():
+    case = latent_small(seed=34, heads=64, d=256, out="f32")
+    c = copy.copy(case)
+    c.comp_indices = np.full_like(case.comp_indices, -1)
+    c.attn_sink = np.full_like(case.attn_sink, -np.inf)
+    announce("latent window only, no sink")
+    got, ref = run(c)
+    compare(got, ref, "bf16", "latent window-only")
+
+
+def test_latent_large_sink_dominates():
+    """A sink far above every score drives the output toward zero without overflow."""
+    case = latent_small(seed=35, heads=32, d=128, out="f32")
+    c = copy.copy(case)
+    c.attn_sink = np.full_like(case.attn_sink, 80.0)
+    announce("latent large sink")
+    got, ref = run(c)
+    assert np.isfinite(to64(got)).all()
+    compare(got, ref, "bf16", "latent large sink")
+
+
+def test_c5_latent_full_size_sampled_rows():
+    """The latent workload at full size (16 decode + 4 x 128 prefill rows, 64 heads,
+    head_dim 512) in the default launch configuration; the oracle checks every
+    decode row and 8 rows of each prefill sequence."""
+    announce("c5 full size: generating")
+    case = W.c5_latent_bf16()
+    off = case.input_row_offsets.astype(np.int64)
+    rows = list(range(16))
+    for b in range(16, case.batch):
+        rows += [int(off[b]), int(off[b]) + 1] + [int(x) for x in np.linspace(off[b] + 2, off[b + 1] - 1, 6)]
+    announce("c5 full size: running (%d rows checked)" % len(rows))
+    got, ref = run(case, rows=rows)
+    compare(got, ref, "bf16", "c5 full", rel_rms_max=0.01)
