@@ -14,13 +14,17 @@ never re-read what the previous one left in L2 or the 256 MiB MALL.
 
 Prints one JSON line: throughput in gathered-KV GB/s (value), query rows/s, the
 fraction of the 8 TB/s HBM peak, a roofline object for the gather kernel timed with
-HIP events around that kernel alone, and the fp64 CPU oracle timed on the host as
-a baseline.
+HIP events around that kernel alone, the fp64 CPU oracle timed on the host as a
+baseline, and the same step measurements for the other workloads (ragged prefill
+with 16 q heads per kv head, block-sparse e4m3 top-16 decode, latent window +
+compressed + sink) under "other_workloads".
 """
 from __future__ import annotations
 
 import argparse
+import copy
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -31,6 +35,35 @@ sys.path.insert(0, ROOT)
 
 METRIC = "gathered-KV GB/s (% of HBM peak) + query-rows/s, bf16 decode config"
 HBM_PEAK_GBPS = 8000.0
+
+
+COUNTERS_SUMMARY = os.path.join(ROOT, "profiles", "gather_valu_c2_decode_bf16_counters.md")
+
+
+def csrc_digest():
+    """sha256 over the library's kernel and host sources (names and contents, sorted)."""
+    d = os.path.join(ROOT, "sparse_attention_ragged_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(d, name), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the gather kernel from the committed FETCH_SIZE/WRITE_SIZE
+    summary, or None when there is none or the sources have changed since it was taken."""
+    if not os.path.exists(COUNTERS_SUMMARY):
+        return None
+    fields = {}
+    for line in open(COUNTERS_SUMMARY):
+        k, sep, v = line.partition(":")
+        if sep and k.strip() in ("traffic_bytes_per_launch", "csrc_sha256"):
+            fields[k.strip()] = v.strip()
+    if fields.get("csrc_sha256") != csrc_digest() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def log(msg):
@@ -66,22 +99,138 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(b))
 
 
-def replicate(dc, R):
-    """R copies of the KV pool at distinct addresses, one page table per copy."""
-    import copy
+def _replicate_leaf(leaf, R):
     import torch
-    kv = dc.kv
-    per = kv.blocks.numel()
-    big = torch.empty(per * R, dtype=kv.blocks.dtype, device=kv.blocks.device)
+    per = leaf.blocks.numel()
+    big = torch.empty(per * R, dtype=leaf.blocks.dtype, device=leaf.blocks.device)
     reps = []
     for k in range(R):
-        big[k * per:(k + 1) * per].copy_(kv.blocks)
-        c = copy.copy(kv)
+        big[k * per:(k + 1) * per].copy_(leaf.blocks)
+        c = copy.copy(leaf)
         c.blocks = big
-        c.num_pages = kv.num_pages * R
-        c.lookup_table = (kv.lookup_table.to(torch.int64) + k * kv.num_pages).to(torch.int32).contiguous()
+        c.num_pages = leaf.num_pages * R
+        c.lookup_table = (leaf.lookup_table.to(torch.int64) + k * leaf.num_pages).to(torch.int32).contiguous()
         reps.append(c)
-    return big, reps
+    return reps
+
+
+def replicate(dc, R):
+    """R device cases whose KV pools (both pools for the latent workload) are copies at
+    distinct addresses, each with its own page table."""
+    kvs = _replicate_leaf(dc.kv, R)
+    comps = _replicate_leaf(dc.comp, R) if dc.comp is not None else [None] * R
+    out = []
+    for k in range(R):
+        c = copy.copy(dc)
+        c.kv, c.comp = kvs[k], comps[k]
+        out.append(c)
+    return out
+
+
+def algorithmic(case):
+    """Per-launch algorithmic work of the gather kernel: gathered K/V bytes, the unit of
+    work with its count and bytes (K/V rows plus the index that names them), and flops
+    (Q.K^T plus P.V, 2 flops per multiply-add)."""
+    import numpy as np
+    import workloads as W
+    eb = W.ELEM_BYTES[case.dtype]
+    D, Hq = case.head_dim, case.num_q_heads
+    gathered = W.gathered_kv_bytes(case)
+    if case.kind == "qsa":
+        units = int(np.clip(case.counts, 0, case.token_indices.shape[1]).sum())
+        per_unit = case.kv.num_kv_heads * 2 * D * eb + 4
+        flops = units * 4 * D * Hq
+        unit = "(query row, selected key): Hkv*2*D*elem K/V bytes + 4 index bytes"
+    elif case.kind == "block_sparse":
+        units = gathered // (2 * D * eb)
+        per_unit = 2 * D * eb
+        flops = units * 4 * D * (Hq // case.kv.num_kv_heads)
+        unit = "(query row, kv head, key in a listed block): 2*D*elem K/V bytes"
+    else:
+        units = gathered // (D * eb)
+        per_unit = D * eb
+        flops = units * 4 * D * Hq
+        unit = "(query row, window or compressed key): D*elem latent bytes"
+    return dict(gathered=gathered, units=int(units), per_unit=per_unit, unit=unit,
+                algo_bytes=int(units) * per_unit, flops=int(flops))
+
+
+def prepare(case, R, dev, opts):
+    """Device-resident inputs (R pool copies when R > 1), workspace and output."""
+    import torch
+    from workloads import device as D
+    dc = D.to_device(case, dev)
+    calls = replicate(dc, R) if R > 1 else [dc]
+    del dc
+    torch.cuda.synchronize()
+    ws_n = D.workspace_size(calls[0], opts)
+    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty(tuple(case.q.shape), dtype=D.out_dtype(case), device=dev)
+    return calls, ws, out
+
+
+def time_steps(calls, opts, out, ws, stream, steps, warmup):
+    """Milliseconds per step over `steps` back-to-back calls (step k uses calls[k % R]),
+    then the gather kernel's average milliseconds from the HIP events the library
+    records around it, over a second pass of `steps` calls."""
+    import torch
+    import sparse_attention_ragged_amd as qsa
+    from workloads import device as D
+    R = len(calls)
+
+    def step(k):
+        D.run(calls[k % R], options=opts, out=out, workspace=ws, stream=stream)
+
+    for k in range(warmup):
+        step(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(k)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    ev = HipEvents(steps)
+    for k in range(steps):
+        qsa.set_timing_events(*ev.pairs[k])
+        step(k)
+    torch.cuda.synchronize()
+    qsa.set_timing_events(None, None)
+    kern = sum(ev.ms(k) for k in range(steps)) / steps
+    ev.close()
+    return ms_step, kern
+
+
+def sampled_parity(case, out, nrows=48):
+    """Max abs difference to the oracle over up to nrows rows spread evenly."""
+    import numpy as np
+    import oracle
+    rows = np.unique(np.linspace(0, case.total_q - 1, min(nrows, case.total_q)).astype(np.int64))
+    ref = oracle.run_case(case, rows=rows)
+    got = out[rows.tolist()].float().cpu().double().numpy()
+    return float(np.abs(got - ref).max())
+
+
+def other_workload(name, make, R, dev, stream, steps, warmup):
+    import torch
+    log("%s: generating" % name)
+    case = make()
+    a = algorithmic(case)
+    calls, ws, out = prepare(case, R, dev, None)
+    log("%s: timing %d steps (+ %d with kernel events)" % (name, steps, steps))
+    ms_step, kern = time_steps(calls, None, out, ws, stream, steps, warmup)
+    res = {"workload": name, "query_rows": case.total_q, "dtype": case.dtype,
+           "gathered_kv_bytes_per_step": a["gathered"], "kv_pool_replicas": R, "steps": steps,
+           "ms_per_step": round(ms_step, 5),
+           "gathered_GBps": round(a["gathered"] / (ms_step * 1e-3) / 1e9, 1),
+           "query_rows_per_s": round(case.total_q / (ms_step * 1e-3), 1),
+           "gather_kernel_avg_us": round(kern * 1e3, 2),
+           "gather_kernel_GBps": round(a["algo_bytes"] / (kern * 1e-3) / 1e9, 1),
+           "gather_kernel_TFLOPs": round(a["flops"] / (kern * 1e-3) / 1e12, 2),
+           "unit_of_work": a["unit"], "units_per_launch": a["units"],
+           "parity_max_abs_sampled_rows": sampled_parity(case, out)}
+    del calls, ws, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(case, budget_s):
@@ -118,6 +267,7 @@ def main():
     ap.add_argument("--unroll", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after warmup, run one device-to-device copy of this many MiB (a kernel "
                          "of known traffic for calibrating hardware byte counters)")
@@ -131,41 +281,20 @@ def main():
     import numpy as np
     import torch
 
-    import sparse_attention_ragged_amd as qsa
     import workloads as W
-    from workloads import device as D
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
     log("generating c2_decode_bf16 (seed 2)")
     case = W.c2_decode_bf16()
-    gathered = W.gathered_kv_bytes(case)
-    units = int(np.clip(case.counts, 0, case.token_indices.shape[1]).sum())   # (row, key) pairs
-    # per (row, selected key): Hkv * 2 * D * 2 bytes of K/V plus a 4-byte index
-    algo_bytes = units * (case.kv.num_kv_heads * 2 * case.head_dim * 2 + 4)
-    log("to device (%.2f GB pool)" % (case.kv.storage.numel() * 2 / 1e9))
-    dc = D.to_device(case, dev)
-    _, reps = replicate(dc, args.replicas)
-    del dc.kv
-    torch.cuda.synchronize()
+    a = algorithmic(case)
+    gathered = a["gathered"]
+    log("to device (%.2f GB pool x %d copies)" % (case.kv.storage.numel() * 2 / 1e9, args.replicas))
     opts = {"num_splits": args.splits, "waves": args.waves, "unroll": args.unroll}
-    stream = torch.cuda.current_stream(dev)
-    ws_n = D.workspace_size(D.DeviceCase(case, dc.q, dc.row_off, reps[0], token_indices=dc.token_indices,
-                                         counts=dc.counts), opts)
-    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
-    out = torch.empty(dc.q.shape, dtype=torch.bfloat16, device=dev)
-    calls = [D.DeviceCase(case, dc.q, dc.row_off, reps[k], token_indices=dc.token_indices,
-                          counts=dc.counts) for k in range(args.replicas)]
-
-    def step(k):
-        D.run(calls[k % args.replicas], options=opts, out=out, workspace=ws, stream=stream)
-
-    log("warmup %d" % args.warmup)
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
+    calls, ws, out = prepare(case, args.replicas, dev, opts)
     if args.copy_probe_mib:
         src = torch.ones(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -173,27 +302,8 @@ def main():
         torch.cuda.synchronize()
         log("copy probe: %d bytes read, %d bytes written" % (src.numel(), dst.numel()))
         del src, dst
-    log("timing %d steps" % args.steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(k)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    # the gather kernel alone: HIP events the library records around it, over the
-    # same number of steps in a second pass (so the timed pass above carries no
-    # event overhead)
-    log("timing the gather kernel with events (%d steps)" % args.steps)
-    ev = HipEvents(args.steps)
-    for k in range(args.steps):
-        qsa.set_timing_events(*ev.pairs[k])
-        step(k)
-    torch.cuda.synchronize()
-    qsa.set_timing_events(None, None)
-    kern_ms = [ev.ms(k) for k in range(args.steps)]
-    ev.close()
-    kern_avg = sum(kern_ms) / len(kern_ms)
+    log("timing %d steps (+ %d with kernel events)" % (args.steps, args.steps))
+    ms_step, kern_avg = time_steps(calls, opts, out, ws, stream, args.steps, args.warmup)
 
     # parity of the last timed output on every row (the oracle takes well under a second)
     import oracle
@@ -202,7 +312,8 @@ def main():
     max_abs = float(np.abs(got - ref).max())
 
     value = gathered / (ms_step * 1e-3) / 1e9
-    achieved = algo_bytes / (kern_avg * 1e-3) / 1e9
+    achieved = a["algo_bytes"] / (kern_avg * 1e-3) / 1e9
+    traffic = measured_traffic()
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -227,11 +338,24 @@ def main():
         "gathered_kv_bytes_per_step": gathered,
         "parity_max_abs_vs_oracle": max_abs,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "gather_valu_kernel<bf16, 128, 4, U>",
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "gather_valu_kernel (bf16, head_dim 128, 4 q heads per kv head, "
+                               "token-index list)",
                      "kernel_avg_us": round(kern_avg * 1e3, 3),
-                     "algorithmic_bytes_per_launch": algo_bytes},
+                     "algorithmic_bytes_per_launch": a["algo_bytes"], "unit_of_work": a["unit"],
+                     "units_per_launch": a["units"], "bytes_per_unit": a["per_unit"],
+                     "traffic_source": "rocprofv3 FETCH_SIZE + WRITE_SIZE per launch, scaled by a "
+                                       "copy of known size; null when the sources changed since"},
     }
+    del calls, ws, out
+    torch.cuda.empty_cache()
+    if not args.no_other_workloads:
+        n = max(5, min(args.steps, 20))
+        res["other_workloads"] = [
+            other_workload("c3_prefill_bf16", W.c3_prefill_bf16, 1, dev, stream, n, 3),
+            other_workload("c4_block_sparse_fp8", W.c4_block_sparse_fp8, 8, dev, stream, n, 3),
+            other_workload("c5_latent_bf16", W.c5_latent_bf16, 4, dev, stream, n, 3),
+        ]
     if not args.no_cpu_baseline:
         log("cpu baseline (~%.0f s)" % args.cpu_seconds)
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
