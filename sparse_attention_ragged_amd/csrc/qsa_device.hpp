@@ -53,14 +53,13 @@ template <> struct Elem<QSA_FP8_E4M3> { static constexpr int bytes = 1; };
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-// binary32 -> bf16 with round-to-nearest-even; NaN stays a (quiet) NaN.
+// binary32 -> bf16 with round-to-nearest-even; NaN stays a (quiet) NaN. Branch-free.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t nan = (u >> 16) | 0x40u;
+    return (u & 0x7fffffffu) > 0x7f800000u ? nan : rne;
 }
 
 // Four OCP E4M3 codes (one dword) -> four floats, exact, via the gfx950 converter.
@@ -93,6 +92,30 @@ __device__ __forceinline__ float team_sum(float x)
     if constexpr (TL >= 32) x += __shfl_xor(x, 16);
     if constexpr (TL >= 64) x += __shfl_xor(x, 32);
     return x;
+}
+
+// Reductions over the lane pairs (l, l^16) and (l, l^32) with the gfx950 row-swap
+// permutes: both operands start as x, and after the swap one holds the partner rows.
+// VALU only (no trip through the LDS queue, unlike a lane shuffle).
+__device__ __forceinline__ float xor16_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Sequence of row r: the b with row_off[b] <= r < row_off[b+1] (binary search; a
@@ -193,19 +216,50 @@ __device__ __forceinline__ KeyPos key_pos(const GatherParams &p, int64_t pos, in
     return k;
 }
 
+// Stage 2 for one leaf: logical page and slot of a position (exact below 2^31), and
+// whether the page table covers it.
+__device__ __forceinline__ const uint32_t *leaf_entry_ptr(const CacheAddr &c, int b, uint64_t t, bool &in,
+                                                          int32_t &slot)
+{
+    const int64_t lp = (int64_t)((t * c.magic) >> c.magic_shift);
+    slot = (int32_t)(t - (uint64_t)lp * (uint64_t)c.page_size);
+    in = lp < c.max_pages;
+    return c.lut + (int64_t)b * c.max_pages + lp;
+}
+
 // Stage 2: address of the page-table entry of k (or a dummy). Updates k.present for
-// positions beyond the page table.
+// positions beyond the page table. Latent keys live in one of two leaves: both
+// addresses are formed and the result selected, so that every leaf field stays a
+// scalar kernel argument (a per-lane choice of leaf would otherwise become a per-lane
+// address into the parameter block, loaded with vector loads).
+template <int LIST>
 __device__ __forceinline__ const uint32_t *page_entry_ptr(const GatherParams &p, int b, KeyPos &k,
                                                           int32_t &slot)
 {
-    const CacheAddr &c = k.comp ? p.comp : p.kv;
     // positions are below 2^31 (int32 lists); larger ones are outside every page table
     k.present = k.present && k.tok < (int64_t(1) << 31);
     const uint64_t t = (uint64_t)(k.tok & 0x7fffffff);
-    const int64_t lp = (int64_t)((t * c.magic) >> c.magic_shift);
-    slot = (int32_t)(t - (uint64_t)lp * (uint64_t)c.page_size);
-    k.present = k.present && lp < c.max_pages;
-    return k.present ? c.lut + (int64_t)b * c.max_pages + lp : c.lut;
+    bool in;
+    const uint32_t *e = leaf_entry_ptr(p.kv, b, t, in, slot);
+    if constexpr (LIST == KEYS_LATENT) {
+        bool in_c;
+        int32_t slot_c;
+        const uint32_t *e_c = leaf_entry_ptr(p.comp, b, t, in_c, slot_c);
+        e = k.comp ? e_c : e;
+        in = k.comp ? in_c : in;
+        slot = k.comp ? slot_c : slot;
+    }
+    k.present = k.present && in;
+    return k.present ? e : p.kv.lut;
+}
+
+// Stage 3 for one leaf: element offset of (page, slot) of the addressed layer.
+__device__ __forceinline__ const char *leaf_row(const CacheAddr &c, uint32_t page, int32_t slot, int64_t head,
+                                                int eb, bool &in)
+{
+    in = (int64_t)page < c.num_pages;
+    const int64_t off = (int64_t)page * c.page_stride + c.layer_off + (int64_t)slot * c.slot_stride + head;
+    return static_cast<const char *>(c.blocks) + off * eb;
 }
 
 // Stage 3: byte address of k's plane-0 row for kv head g (or `dummy`).
@@ -213,11 +267,17 @@ template <int EB, int LIST>
 __device__ __forceinline__ const char *row_address(const GatherParams &p, const KeyPos &k, uint32_t page,
                                                    int32_t slot, int g, const char *dummy, bool &present)
 {
-    const CacheAddr &c = k.comp ? p.comp : p.kv;
-    present = k.present && (int64_t)page < c.num_pages;
     const int64_t head = LIST == KEYS_LATENT ? 0 : (int64_t)g * p.head_dim;
-    const int64_t off = (int64_t)page * c.page_stride + c.layer_off + (int64_t)slot * c.slot_stride + head;
-    return present ? static_cast<const char *>(c.blocks) + off * EB : dummy;
+    bool in;
+    const char *a = leaf_row(p.kv, page, slot, head, EB, in);
+    if constexpr (LIST == KEYS_LATENT) {
+        bool in_c;
+        const char *a_c = leaf_row(p.comp, page, slot, head, EB, in_c);
+        a = k.comp ? a_c : a;
+        in = k.comp ? in_c : in;
+    }
+    present = k.present && in;
+    return present ? a : dummy;
 }
 
 // Normalising factor of a finished softmax state (reference M, sum L, log2 domain):

@@ -151,7 +151,7 @@ __global__ void __launch_bounds__(64 * kMfmaMaxWaves) gather_mfma_kernel(GatherP
         for (int h = 0; h < 2; ++h) {
             const int64_t jj = key_index(batch, h);
             P.k[h] = key_pos<LIST>(p, pos, jj, E.raw[h], jj < j1);
-            P.page[h] = *page_entry_ptr(p, b, P.k[h], P.slot[h]);
+            P.page[h] = *page_entry_ptr<LIST>(p, b, P.k[h], P.slot[h]);
         }
     };
     auto load_rows = [&](const Pages &P, Rows &R) {

@@ -1,17 +1,29 @@
 // Latent gather-attention on matrix cores for wide head groups ("latent_sparse_attention_
 // ragged_paged": one latent head whose row is both key and value, many query heads).
 //
-// One workgroup owns one (query row, split) and has one wavefront per tile of 16 query
-// heads (up to 64 heads, head_dim up to 512). The keys of the split (window positions,
-// then listed compressed entries) go through the three-stage address pipeline and
-// arrive 32 at a time in an LDS tile that all wavefronts share; the next tile's rows
-// are in flight while the current one is used (two LDS buffers, one barrier per tile).
-// Each wavefront then runs, on 16x16x32 MFMAs,
-//   S^T = X . Q^T    (A: 8 dims of key i from LDS, B: its heads' q rows, held in VGPRs)
-//   online softmax per head in the log2 domain (lazy rescale as in the other kernels)
-//   O^T += X^T P^T   (A: transposing LDS reads of the same tile, B: P^T straight from
-//                     the S^T accumulators)
-// and owns its heads' whole output rows, so no cross-wave merge is needed. The per-head
+// One workgroup owns one (query row, split): 64 query heads in four tiles of 16 (heads
+// past the group compute on zero queries and are not stored), keys 32 at a time. Its
+// eight wavefronts take two roles, one of each per SIMD:
+//
+//  * score wavefront s (heads 16s..16s+15) computes, on 16x16x32 MFMAs,
+//    S^T = X . Q^T (A: 8 dims of a key from the LDS key tile, B: the heads' q rows,
+//    held in VGPRs), and runs the online softmax for its heads in the log2 domain
+//    (lazy rescale), leaving P (bf16, already in the MFMA operand layout) and the
+//    rescale factors in LDS;
+//  * value wavefront s accumulates O^T += X^T P^T for the same heads one tile later
+//    (A: transposing LDS reads of the key tile, B: P from LDS) and owns their output
+//    rows.
+//
+// All eight wavefronts also load: each walks its share of the keys of the split
+// (window positions, then listed compressed entries) through the three-stage address
+// pipeline and writes its chunks of their latent rows into an LDS key tile. Per tile:
+// every wavefront stores its chunks of tile t+1 and issues loads, then score
+// wavefronts score tile t while value wavefronts accumulate tile t-1; one barrier,
+// which waits only for LDS traffic, ends the step (three LDS key tiles, two P
+// buffers). The vector-memory counter retires loads in issue order, so the three
+// address stages run DEPTH, 2*DEPTH and 3*DEPTH tiles ahead (rows, page-table
+// entries, list entries) and no step waits for anything newer than the tile it
+// stores. LDS operand reads are software-pipelined a few MFMAs ahead. The per-head
 // sink logit joins the denominator once, at the final normalisation (here with one
 // split, in the combine kernel otherwise).
 #include "qsa_device.hpp"
@@ -25,10 +37,14 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 
-constexpr int kWideMaxWaves = 4;      // 64 heads
+constexpr int kWaves = 4;             // head tiles (64 heads); one score + one value wavefront each
 constexpr int kWTile = 32;            // keys per tile
+constexpr int kDepth = 2;             // tiles of rows in flight
+constexpr int kXBufs = 3;             // LDS key tiles: being written, scored, accumulated
+constexpr int kUnroll = 6;            // steps per loop trip: register slots and LDS tiles static
 constexpr float kWSlack = 8.0f;
-constexpr int kWThreads = 64 * kWideMaxWaves;
+constexpr int kPrefetch = 4;          // MFMA steps of LDS operand reads kept in flight
+constexpr int kWThreads = 64 * 2 * kWaves;
 
 __device__ __forceinline__ bf16x8_t wide_bf16x8(u32x4 v)
 {
@@ -37,243 +53,355 @@ __device__ __forceinline__ bf16x8_t wide_bf16x8(u32x4 v)
     return r;
 }
 
-template <int D, int WAVES>
-__global__ void __launch_bounds__(kWThreads) gather_mfma_wide_kernel(GatherParams p)
+// Workgroup barrier that orders LDS accesses only: global loads stay in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Four consecutive outputs of one head: bf16 (round to nearest even) or fp32.
+__device__ __forceinline__ void store_out4(void *out, int32_t out_dtype, int64_t idx, f32x4_t v)
+{
+    if (out_dtype == QSA_BF16) {
+        typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+        const u32x2v w = {f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
+                          f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16)};
+        *reinterpret_cast<u32x2v *>(static_cast<uint16_t *>(out) + idx) = w;
+    } else {
+        *reinterpret_cast<f32x4_t *>(static_cast<float *>(out) + idx) = v;
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gather_mfma_wide_kernel(GatherParams p)
 {
     constexpr int EB = 2;                       // bf16
     constexpr int NC = D / 32;
     constexpr int NDT = D / 16;
-    constexpr int ROW = D + 8;                  // LDS row (bf16 elements), +16 B against bank conflicts
+    // LDS row (bf16 elements): 32 bytes of padding keep both the 16-byte row reads of
+    // the score step and the transposing reads of the value step free of bank conflicts
+    constexpr int ROW = D + 16;
     constexpr int CHUNKS = D * EB / 16;         // 16-byte chunks of one row
     static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
-    __shared__ __attribute__((aligned(16))) uint16_t s_x[2][kWTile * ROW];
-    __shared__ uint32_t s_ok[2];
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[kXBufs][kWTile * ROW];
+    __shared__ __attribute__((aligned(16))) u32x4 s_p[2][kWaves][64];   // P^T operands
+    __shared__ float s_alpha[2][kWaves][16];    // rescale factor per head (when flagged)
+    __shared__ uint32_t s_flag[2][kWaves];      // 1: the value wavefront rescales before adding
+    __shared__ uint32_t s_ok[kXBufs][2 * kWaves];   // presence bits of each wavefront's keys
+    __shared__ float s_ml[kWaves][16][2];       // final (reference, sum) per head
+
+    // loading layout: TPK threads per key, each loading CPT chunks (chunk u*TPK + sub);
+    // wavefront w stages keys KPW*w .. KPW*w + KPW-1 of a tile
+    constexpr int TPK = kWThreads / kWTile;
+    constexpr int CPT = CHUNKS / TPK;
+    constexpr int KPW = 64 / TPK;
+    static_assert(CHUNKS % TPK == 0, "row chunks must split evenly over a key's threads");
 
     const int S = p.num_splits;
     const int G = p.group;
     const int s = (int)(blockIdx.x % S);
     const int64_t r = blockIdx.x / S;
     const int tid = threadIdx.x;
-    const int nthreads = blockDim.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int li = lane & 15;
     const int lq = lane >> 4;
-
-    // staging layout: tpk threads per key, each loading cpt chunks (chunk u*tpk + sub)
-    constexpr int tpk = 64 * WAVES / kWTile;
-    constexpr int cpt = CHUNKS / tpk;
-    static_assert(CHUNKS % tpk == 0, "row chunks must split evenly over a key's threads");
-    const int skey = tid / tpk;
-    const int ssub = tid % tpk;
-    (void)nthreads;
-
-    // prologue
-    const int64_t n = key_list_length(p, r);
-    const int head = 16 * wave + li;            // within the group
+    const int hw = wave % kWaves;               // head tile of this wavefront
+    const int head = 16 * hw + li;              // within the group
     const bool head_real = head < G;
-    const char *qrow0 = static_cast<const char *>(p.q) + (r * p.num_q_heads) * D * EB;
-    const char *qrow = head_real ? qrow0 + (int64_t)head * D * EB : qrow0;
-    u32x4 qf[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const u32x4 v = ldg16(qrow + (32 * c + 8 * lq) * EB);
-        qf[c] = head_real ? v : u32x4{0, 0, 0, 0};
-    }
-    const int b = find_seq_wave(p.row_off, p.batch, (uint32_t)r);
-    const int64_t pos = (int64_t)p.cache_lengths[b] + (r - (int64_t)p.row_off[b]);
+
+    const int64_t n = key_list_length(p, r);
     const int64_t j0 = (int64_t)s * p.split_keys;
     const int64_t j1 = n < j0 + p.split_keys ? n : j0 + p.split_keys;
     const int nb = j1 > j0 ? (int)((j1 - j0 + kWTile - 1) / kWTile) : 0;
-    const char *dummy = qrow0;
+    // steps: nb scores, then the value step of the last tile; a whole number of loop
+    // trips so that register slots and LDS tiles stay static (extra steps idle)
+    const int nsteps = nb > 0 ? (nb + 1 + kUnroll - 1) / kUnroll * kUnroll : 0;
+    const char *qrow0 = static_cast<const char *>(p.q) + (r * p.num_q_heads) * D * EB;
 
-    float m = kNoKey, lsum = 0.f;
-    f32x4_t acc[NDT];
-#pragma unroll
-    for (int t = 0; t < NDT; ++t)
-        acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    struct Entry { int32_t raw; };
-    struct Page { KeyPos k; int32_t slot; uint32_t page; };
-    struct Rows { u32x4 x[cpt]; bool ok; };
-
-    auto key_index = [&](int tile) -> int64_t { return j0 + (int64_t)tile * kWTile + skey; };
-    auto load_entry = [&](int tile, Entry &E) {
-        const int64_t jj = key_index(tile);
-        E.raw = *entry_ptr<KEYS_LATENT>(p, r, 0, jj, jj < j1);
-    };
-    auto load_page = [&](int tile, const Entry &E, Page &P) {
-        const int64_t jj = key_index(tile);
-        P.k = key_pos<KEYS_LATENT>(p, pos, jj, E.raw, jj < j1);
-        P.page = *page_entry_ptr(p, b, P.k, P.slot);
-    };
-    auto load_rows = [&](const Page &P, Rows &R) {
-        bool ok;
-        const char *a = row_address<EB, KEYS_LATENT>(p, P.k, P.page, P.slot, 0, dummy, ok);
-        R.ok = ok;
-        const char *base = ok ? a : dummy;
-#pragma unroll
-        for (int u = 0; u < cpt; ++u)
-            R.x[u] = ldg16(base + (int64_t)(u * tpk + ssub) * 16);
-    };
-    auto store_rows = [&](const Rows &R, int buf) {
-        uint16_t *row = s_x[buf] + skey * ROW;
-#pragma unroll
-        for (int u = 0; u < cpt; ++u)
-            *reinterpret_cast<u32x4 *>(row + (u * tpk + ssub) * 8) = R.x[u];
-        if (ssub == 0) {
-            const unsigned long long bal = __ballot(R.ok);
-            // keys of this wavefront: lanes 0, tpk, 2 tpk, ... hold them in order
-            uint32_t bits = 0;
-            for (int k = 0; k < 64 / tpk; ++k)
-                bits |= (uint32_t)((bal >> (k * tpk)) & 1ull) << k;
-            if (lane == 0)
-                atomicOr(&s_ok[buf], bits << (wave * (64 / tpk)));
-        }
-    };
-    auto compute = [&](int buf) {
-        const uint16_t *x = s_x[buf];
-        const uint32_t present = s_ok[buf];
-        f32x4_t st[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            st[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const u32x4 kf = *reinterpret_cast<const u32x4 *>(x + (16 * h + li) * ROW + 32 * c + 8 * lq);
-                st[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wide_bf16x8(kf), wide_bf16x8(qf[c]), st[h], 0,
-                                                                0, 0);
-            }
-        }
-        float sc[2][4];
-        float mx = m;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = 16 * h + 4 * lq + i;
-                const float v = st[h][i] * p.scale_log2;
-                sc[h][i] = (present >> key) & 1u ? v : kNegInf;
-                mx = fmaxf(mx, sc[h][i]);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (__any(mx > m + kWSlack)) {
-            const float alpha = __builtin_amdgcn_exp2f(m - mx);
-            lsum *= alpha;
-#pragma unroll
-            for (int t = 0; t < NDT; ++t)
-                acc[t] *= alpha;
-            m = mx;
-        }
-        float w[2][4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                w[h][i] = __builtin_amdgcn_exp2f(sc[h][i] - m);
-                lsum += w[h][i];
-            }
-        const u32x4 pb = {pack_bf16x2(w[0][0], w[0][1]), pack_bf16x2(w[0][2], w[0][3]),
-                          pack_bf16x2(w[1][0], w[1][1]), pack_bf16x2(w[1][2], w[1][3])};
-        const int jr = li >> 2, qd = li & 3;
-#pragma unroll
-        for (int t = 0; t < NDT; ++t) {
-            const int col = 16 * t + 4 * qd;
-            const s16x4_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4 *)(x + (4 * lq + jr) * ROW + col));
-            const s16x4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4 *)(x + (16 + 4 * lq + jr) * ROW + col));
-            u32x4 av;
-            __builtin_memcpy(&av, &a0, 8);
-            __builtin_memcpy(reinterpret_cast<char *>(&av) + 8, &a1, 8);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wide_bf16x8(av), wide_bf16x8(pb), acc[t], 0, 0, 0);
-        }
-    };
-
-    if (nb > 0) {
-        Entry E0, E1;
-        Page P0, P1;
-        Rows R;
-        if (tid < 2)
-            s_ok[tid] = 0;
-        __syncthreads();
-        load_entry(0, E0);
-        load_entry(1, E1);
-        load_page(0, E0, P0);
-        load_rows(P0, R);
-        load_entry(2, E0);
-        load_page(1, E1, P1);
-        store_rows(R, 0);
-        __syncthreads();
-        // iteration i: rows(i+1) in flight while tile i is used; entries / pages run
-        // two / one tiles ahead of the rows
-        for (int i = 0; i < nb; i += 2) {
-            load_rows(P1, R);                   // tile i+1
-            load_entry(i + 3, E1);
-            load_page(i + 2, E0, P0);
-            compute(0);
-            __syncthreads();                    // every wavefront is done with buffer 0
-            if (tid == 0)
-                s_ok[0] = 0;
-            store_rows(R, 1);
-            __syncthreads();
-            if (i + 1 >= nb)
-                break;
-            load_rows(P0, R);                   // tile i+2
-            load_entry(i + 4, E0);
-            load_page(i + 3, E1, P1);
-            compute(1);
-            __syncthreads();
-            if (tid == 0)
-                s_ok[1] = 0;
-            store_rows(R, 0);
-            __syncthreads();
-        }
-    }
-
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    const int64_t gh = (int64_t)head;           // the single kv head: group = all q heads
-    if (head_real) {
+    const bool is_score = wave >= kWaves;
+    // normalised output rows of this wavefront's heads (one split) or the split's partial
+    auto finish = [&](float m, float lsum, const f32x4_t *acc) {
+        const int64_t gh = (int64_t)head;       // the single kv head: group = all q heads
+        if (!head_real)
+            return;
         const int64_t rh = r * p.num_q_heads + gh;
         if (S == 1) {
             const float inv = final_factor(p, gh, m, lsum);
 #pragma unroll
             for (int t = 0; t < NDT; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    store_out(p.out, p.out_dtype, rh * D + 16 * t + 4 * lq + i, acc[t][i] * inv);
+                store_out4(p.out, p.out_dtype, rh * D + 16 * t + 4 * lq, acc[t] * inv);
         } else {
             const int64_t srh = (int64_t)s * p.total_q * p.num_q_heads + rh;
 #pragma unroll
             for (int t = 0; t < NDT; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    p.ws_acc[srh * D + 16 * t + 4 * lq + i] = acc[t][i];
+                *reinterpret_cast<f32x4_t *>(p.ws_acc + srh * D + 16 * t + 4 * lq) = acc[t];
             if (lq == 0) {
                 p.ws_ml[srh * 2] = m;
                 p.ws_ml[srh * 2 + 1] = lsum;
             }
         }
+    };
+    if (nb == 0) {                              // no keys: zeros (or an empty partial)
+        if (!is_score) {
+            f32x4_t zero[NDT];
+#pragma unroll
+            for (int t = 0; t < NDT; ++t)
+                zero[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            finish(kNoKey, 0.f, zero);
+        }
+        return;
+    }
+    {
+        const int b = find_seq_wave(p.row_off, p.batch, (uint32_t)r);
+        const int64_t pos = (int64_t)p.cache_lengths[b] + (r - (int64_t)p.row_off[b]);
+        const char *dummy = qrow0;
+        const int skey = tid / TPK;
+        const int ssub = tid % TPK;
+
+        struct Page { KeyPos k; int32_t slot; uint32_t page; };
+        struct Rows { u32x4 x[CPT]; bool ok; };
+
+        auto key_index = [&](int tile) -> int64_t { return j0 + (int64_t)tile * kWTile + skey; };
+        auto load_entry = [&](int tile) -> int32_t {
+            const int64_t jj = key_index(tile);
+            return *entry_ptr<KEYS_LATENT>(p, r, 0, jj, jj < j1);
+        };
+        auto load_page = [&](int tile, int32_t raw, Page &P) {
+            const int64_t jj = key_index(tile);
+            P.k = key_pos<KEYS_LATENT>(p, pos, jj, raw, jj < j1);
+            P.page = *page_entry_ptr<KEYS_LATENT>(p, b, P.k, P.slot);
+        };
+        auto load_rows = [&](const Page &P, Rows &R) {
+            bool ok;
+            const char *a = row_address<EB, KEYS_LATENT>(p, P.k, P.page, P.slot, 0, dummy, ok);
+            R.ok = ok;
+            const char *base = ok ? a : dummy;
+#pragma unroll
+            for (int u = 0; u < CPT; ++u)
+                R.x[u] = ldg16(base + (int64_t)(u * TPK + ssub) * 16);
+        };
+        // rows -> LDS tile `buf`, presence bits -> s_ok[buf][wave]; visible after the next barrier
+        auto store_rows = [&](const Rows &R, int buf) {
+            uint16_t *row = s_x[buf] + skey * ROW;
+#pragma unroll
+            for (int u = 0; u < CPT; ++u)
+                *reinterpret_cast<u32x4 *>(row + (u * TPK + ssub) * 8) = R.x[u];
+            const unsigned long long bal = __ballot(R.ok);
+            uint32_t bits = 0;
+#pragma unroll
+            for (int k = 0; k < KPW; ++k)
+                bits |= (uint32_t)((bal >> (k * TPK)) & 1ull) << k;
+            if (lane == 0)
+                s_ok[buf][wave] = bits;
+        };
+
+
+        // `xb`: the LDS key tile holding `tile`, tile % 3 (a compile-time constant in the
+        // unrolled steps)
+        auto accumulate = [&](int tile, int xb, f32x4_t *acc) {
+            const int pb_buf = tile & 1;
+            if (s_flag[pb_buf][hw]) {
+                const float alpha = s_alpha[pb_buf][hw][li];
+#pragma unroll
+                for (int t = 0; t < NDT; ++t)
+                    acc[t] *= alpha;
+            }
+            const u32x4 pb = s_p[pb_buf][hw][lane];
+            const uint16_t *x = s_x[xb];
+            const int jr = li >> 2, qd = li & 3;
+            // A = X^T for 16 dims x 32 keys: two transposing reads (keys 4q..4q+3 and
+            // 16+4q..16+4q+3 of dims 16t+4qd..+3)
+            auto read_a = [&](int t) {
+                const int col = 16 * t + 4 * qd;
+                const s16x4_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4 *)(x + (4 * lq + jr) * ROW + col));
+                const s16x4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4 *)(x + (16 + 4 * lq + jr) * ROW + col));
+                u32x4 av;
+                __builtin_memcpy(&av, &a0, 8);
+                __builtin_memcpy(reinterpret_cast<char *>(&av) + 8, &a1, 8);
+                return av;
+            };
+            // software pipeline: the reads of step t+PF are issued before the MFMA of
+            // step t (scheduling fences keep the order)
+            u32x4 av[kPrefetch];
+#pragma unroll
+            for (int t = 0; t < kPrefetch; ++t)
+                av[t] = read_a(t);
+#pragma unroll
+            for (int t = 0; t < NDT; ++t) {
+                const u32x4 a = av[t % kPrefetch];
+                if (t + kPrefetch < NDT)
+                    av[t % kPrefetch] = read_a(t + kPrefetch);
+                __builtin_amdgcn_sched_barrier(0);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wide_bf16x8(a), wide_bf16x8(pb), acc[t], 0, 0, 0);
+            }
+        };
+
+        auto score = [&](int tile, int xb, const u32x4 *qf, float &m, float &lsum) {
+            const uint16_t *x = s_x[xb];
+            uint32_t present = 0;
+#pragma unroll
+            for (int w = 0; w < 2 * kWaves; ++w)
+                present |= s_ok[xb][w] << (w * KPW);
+            // two chains per key half (even / odd 32-dim chunks) halve the MFMA dependency depth
+            f32x4_t st[2], st2[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                st[h] = st2[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            // A = 16 keys x 32 dims of X (keys 16h + i), one 16-byte read per lane;
+            // software-pipelined like the value step
+            auto read_k = [&](int c, int h) {
+                return *reinterpret_cast<const u32x4 *>(x + (16 * h + li) * ROW + 32 * c + 8 * lq);
+            };
+            u32x4 kf[kPrefetch][2];
+#pragma unroll
+            for (int c = 0; c < kPrefetch; ++c) {
+                kf[c][0] = read_k(c, 0);
+                kf[c][1] = read_k(c, 1);
+            }
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const u32x4 k0 = kf[c % kPrefetch][0], k1 = kf[c % kPrefetch][1];
+                if (c + kPrefetch < NC) {
+                    kf[c % kPrefetch][0] = read_k(c + kPrefetch, 0);
+                    kf[c % kPrefetch][1] = read_k(c + kPrefetch, 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                f32x4_t *sa = c & 1 ? st2 : st;
+                sa[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wide_bf16x8(k0), wide_bf16x8(qf[c]), sa[0], 0, 0, 0);
+                sa[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wide_bf16x8(k1), wide_bf16x8(qf[c]), sa[1], 0, 0, 0);
+            }
+            st[0] += st2[0];
+            st[1] += st2[1];
+            float sc[2][4];
+            float mx = m;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = 16 * h + 4 * lq + i;
+                    const float v = st[h][i] * p.scale_log2;
+                    sc[h][i] = (present >> key) & 1u ? v : kNegInf;
+                    mx = fmaxf(mx, sc[h][i]);
+                }
+            mx = xor32_max(xor16_max(mx));
+            const int pb_buf = tile & 1;
+            uint32_t flag = 0;
+            if (__any(mx > m + kWSlack)) {
+                const float alpha = __builtin_amdgcn_exp2f(m - mx);
+                lsum *= alpha;
+                m = mx;
+                if (lq == 0)
+                    s_alpha[pb_buf][hw][li] = alpha;
+                flag = 1;
+            }
+            if (lane == 0)
+                s_flag[pb_buf][hw] = flag;
+            float w[2][4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    w[h][i] = __builtin_amdgcn_exp2f(sc[h][i] - m);
+                    lsum += w[h][i];
+                }
+            s_p[pb_buf][hw][lane] = u32x4{pack_bf16x2(w[0][0], w[0][1]), pack_bf16x2(w[0][2], w[0][3]),
+                                          pack_bf16x2(w[1][0], w[1][1]), pack_bf16x2(w[1][2], w[1][3])};
+        };
+
+        // pipeline fill: list entries of tiles 0..3*DEPTH, page entries of 0..2*DEPTH,
+        // rows of 0..DEPTH (issue order = retirement order)
+        int32_t E[kDepth];
+        Page P[kDepth];
+        Rows R[kDepth];
+        int32_t e_fill[3 * kDepth + 1];
+#pragma unroll
+        for (int j = 0; j <= 3 * kDepth; ++j)
+            e_fill[j] = load_entry(j);
+        Page p_fill[2 * kDepth + 1];
+#pragma unroll
+        for (int j = 0; j <= 2 * kDepth; ++j)
+            load_page(j, e_fill[j], p_fill[j]);
+        Rows r0;
+        load_rows(p_fill[0], r0);
+#pragma unroll
+        for (int j = 1; j <= kDepth; ++j)
+            load_rows(p_fill[j], R[j % kDepth]);
+        // steady-state registers before step t: R[j % DEPTH] holds the rows of tiles
+        // t+1 .. t+DEPTH, P[j % DEPTH] the page entries of t+1+DEPTH .. t+2*DEPTH and
+        // E[j % DEPTH] the list entries of t+1+2*DEPTH .. t+3*DEPTH
+#pragma unroll
+        for (int j = kDepth + 1; j <= 2 * kDepth; ++j)
+            P[j % kDepth] = p_fill[j];
+#pragma unroll
+        for (int j = 2 * kDepth + 1; j <= 3 * kDepth; ++j)
+            E[j % kDepth] = e_fill[j];
+        store_rows(r0, 0);
+        lds_barrier();
+
+        // the steps; each role runs its own copy of the loop so that only its own state
+        // is live in it. A store past the last tile writes a tile buffer nobody reads.
+        static_assert(kUnroll % kDepth == 0 && kUnroll % kXBufs == 0, "static slots need a common period");
+        auto steps = [&](auto &&work) {
+            for (int t = 0; t < nsteps; t += kUnroll) {
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const int tt = t + u;
+                    const int k = (u + 1) % kDepth;  // register slot of tiles tt+1 (+ multiples of DEPTH)
+                    store_rows(R[k], (u + 1) % kXBufs);              // tile tt+1 -> LDS tile (tt+1) % 3
+                    load_rows(P[k], R[k]);                           // rows of tt+1+DEPTH
+                    load_page(tt + 1 + 2 * kDepth, E[k], P[k]);      // pages of tt+1+2*DEPTH
+                    E[k] = load_entry(tt + 1 + 3 * kDepth);          // entries of tt+1+3*DEPTH
+                    work(tt, u);
+                    lds_barrier();
+                }
+            }
+        };
+        if (is_score) {
+            // B operand of S^T: 8 dims of this lane's head per 32-dim chunk (zeros for padding heads)
+            const char *qrow = qrow0 + (int64_t)(head_real ? head : 0) * D * EB;
+            u32x4 qf[NC];
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const u32x4 v = ldg16(qrow + (32 * c + 8 * lq) * EB);
+                qf[c] = head_real ? v : u32x4{0, 0, 0, 0};
+            }
+            float m = kNoKey, lsum = 0.f;
+            steps([&](int tt, int u) {
+                if (tt < nb)
+                    score(tt, u % kXBufs, qf, m, lsum);
+            });
+            lsum = xor32_sum(xor16_sum(lsum));
+            if (lq == 0) {
+                s_ml[hw][li][0] = m;
+                s_ml[hw][li][1] = lsum;
+            }
+            lds_barrier();
+            return;
+        }
+        f32x4_t acc[NDT];
+#pragma unroll
+        for (int t = 0; t < NDT; ++t)
+            acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        steps([&](int tt, int u) {
+            if (tt >= 1 && tt <= nb)
+                accumulate(tt - 1, (u + kXBufs - 1) % kXBufs, acc);
+        });
+        lds_barrier();                          // the score wavefronts' final state
+        finish(s_ml[hw][li][0], s_ml[hw][li][1], acc);
     }
 }
 
 template <int D>
 int launch_wide(const GatherParams &p, void *stream)
 {
-    // one wavefront per 16 heads, rounded up to 2 or 4 wavefronts (padded heads idle)
     const int64_t grid = p.total_q * (int64_t)p.num_splits;
     if (grid <= 0)
         return 0;
     if (grid > 0x7fffffff)
         return (int)hipErrorInvalidConfiguration;
-    if (p.group <= 32)
-        hipLaunchKernelGGL((gather_mfma_wide_kernel<D, 2>), dim3((unsigned)grid), dim3(128), 0,
-                           static_cast<hipStream_t>(stream), p);
-    else
-        hipLaunchKernelGGL((gather_mfma_wide_kernel<D, 4>), dim3((unsigned)grid), dim3(256), 0,
-                           static_cast<hipStream_t>(stream), p);
+    hipLaunchKernelGGL((gather_mfma_wide_kernel<D>), dim3((unsigned)grid), dim3(kWThreads), 0,
+                       static_cast<hipStream_t>(stream), p);
     return (int)hipGetLastError();
 }
 
@@ -281,7 +409,7 @@ int launch_wide(const GatherParams &p, void *stream)
 
 bool mfma_wide_supported(int32_t dtype, int32_t group, int32_t head_dim, int32_t list_kind)
 {
-    return dtype == QSA_BF16 && list_kind == KEYS_LATENT && group > 16 && group <= 16 * kWideMaxWaves &&
+    return dtype == QSA_BF16 && list_kind == KEYS_LATENT && group > 16 && group <= 16 * kWaves &&
            (head_dim == 128 || head_dim == 256 || head_dim == 512);
 }
 

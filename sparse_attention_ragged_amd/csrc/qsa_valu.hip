@@ -120,7 +120,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParam
         for (int u = 0; u < U; ++u) {
             const int64_t jj = key_index(batch, u);
             P.k[u] = key_pos<LIST>(p, pos, jj, E.raw[u], jj < j1);
-            P.page[u] = *page_entry_ptr(p, b, P.k[u], P.slot[u]);
+            P.page[u] = *page_entry_ptr<LIST>(p, b, P.k[u], P.slot[u]);
         }
     };
     auto load_rows = [&](const Pages &P, Rows &R) {
