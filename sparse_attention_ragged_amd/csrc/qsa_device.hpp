@@ -118,6 +118,30 @@ __device__ __forceinline__ float xor32_sum(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// The value of lane l and of its partner lane l^OFF, as an unordered pair (a, b): one
+// of the two is this lane's own value. Symmetric combinations (sums, maxima, softmax
+// merges) can use the pair directly. 8: DPP row rotation; 16 and 32: gfx950 row-swap
+// permutes; other offsets fall back to a lane shuffle.
+template <int OFF>
+__device__ __forceinline__ void xor_pair(float x, float &a, float &b)
+{
+    if constexpr (OFF == 8) {
+        a = x;
+        b = dpp_f<0x128>(x);                    // row_ror:8 = lane ^ 8 within a 16-lane row
+    } else if constexpr (OFF == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        a = __uint_as_float(r[0]);
+        b = __uint_as_float(r[1]);
+    } else if constexpr (OFF == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        a = __uint_as_float(r[0]);
+        b = __uint_as_float(r[1]);
+    } else {
+        a = x;
+        b = __shfl_xor(x, OFF);
+    }
+}
+
 // Sequence of row r: the b with row_off[b] <= r < row_off[b+1] (binary search; a
 // chain of dependent loads, used only for very large batches).
 __device__ __forceinline__ int find_seq(const uint32_t *row_off, int batch, uint32_t r)
@@ -293,6 +317,16 @@ __device__ __forceinline__ float final_factor(const GatherParams &p, int64_t hea
         L = L * c + __builtin_amdgcn_exp2f(sl - M2);
     }
     return L > 0.f ? c / L : 0.f;
+}
+
+// Two adjacent outputs (idx even): one 4-byte bf16 pair or one 8-byte float pair.
+__device__ __forceinline__ void store_out2(void *out, int32_t out_dtype, int64_t idx, float v0, float v1)
+{
+    if (out_dtype == QSA_BF16)
+        *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(out) + idx) =
+            f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+    else
+        *reinterpret_cast<float2 *>(static_cast<float *>(out) + idx) = make_float2(v0, v1);
 }
 
 __device__ __forceinline__ void store_out(void *out, int32_t out_dtype, int64_t idx, float v)

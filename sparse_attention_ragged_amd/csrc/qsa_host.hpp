@@ -66,6 +66,7 @@ struct GatherParams {
     int32_t waves;
     int32_t unroll;
     int64_t split_keys;              // keys per split (in key-list units)
+    int32_t head_block;              // wavefront kernel: kv heads one workgroup covers
     float *ws_acc;                   // [S, total_q, Hq, D] when num_splits > 1
     float *ws_ml;                    // [S, total_q, Hq, 2]
 };
@@ -83,9 +84,22 @@ struct Plan {
     int32_t unroll;
     int64_t key_capacity;   // upper bound of keys per (row, kv head)
     int64_t split_keys;
+    int32_t head_block;     // wavefront kernel: kv heads per workgroup (1 for other paths)
     size_t ws_bytes;
     size_t ws_ml_offset;
 };
+
+// Team layout of the wavefront kernel, shared by the kernel and the planner: a key's
+// K (or V) row of one kv head is split over a team of lanes, each holding one or two
+// 16-byte chunks (two where a lane then holds at most 16 elements).
+constexpr int valu_chunks_per_lane(int elem_bytes, int head_dim)
+{
+    return head_dim * elem_bytes >= 64 && 2 * (16 / elem_bytes) <= 16 ? 2 : 1;
+}
+constexpr int valu_team_lanes(int elem_bytes, int head_dim)
+{
+    return head_dim * elem_bytes / (16 * valu_chunks_per_lane(elem_bytes, head_dim));
+}
 
 // Validation + planning (qsa_plan.cpp). They never touch the device.
 qsa_status check_cache(const qsa_paged_cache *c, const char *what, int64_t planes);

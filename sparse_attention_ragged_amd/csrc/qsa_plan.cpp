@@ -141,8 +141,25 @@ qsa_status plan_gather(const qsa_ragged_q *q, int64_t num_kv_heads, int32_t dtyp
     plan->unroll = o.unroll ? o.unroll : 4;
     plan->key_capacity = key_capacity;
 
+    // wavefront kernel: when every kv head reads the same keys and there are too few
+    // (row, kv head) items to fill the device without splitting, one workgroup covers a
+    // block of kv heads (one team each): a wavefront then reads all of a key's heads at
+    // once and computes the key's address once. With enough items, one kv head per
+    // workgroup needs no split-K partials (measured faster on the decode workload,
+    // where the combine step costs more than the shared addressing saves).
+    plan->head_block = 1;
+    if (plan->path == PATH_VALU && list_kind != KEYS_BLOCKS && q->total_q * num_kv_heads < kTargetWorkgroups) {
+        const int eb = dtype == QSA_F32 ? 4 : dtype == QSA_BF16 ? 2 : 1;
+        int64_t a = num_kv_heads, c = 64 / valu_team_lanes(eb, Dh);
+        while (c) {
+            const int64_t t = a % c;
+            a = c;
+            c = t;
+        }
+        plan->head_block = (int32_t)a;  // gcd(kv heads, teams per wavefront)
+    }
     const int64_t cap = key_capacity > 0 ? key_capacity : 1;
-    const int64_t items = q->total_q * num_kv_heads;
+    const int64_t items = q->total_q * (num_kv_heads / plan->head_block);
     int64_t splits = o.num_splits;
     if (splits == 0) {
         splits = items > 0 ? ceil_div(kTargetWorkgroups, items) : 1;

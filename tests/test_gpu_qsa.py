@@ -184,10 +184,13 @@ def test_page_permutation_and_poison_are_bitwise_invariant():
     assert torch.equal(base, out3), "entries past counts were read"
 
 
-@pytest.mark.parametrize("dtype,agree", [("f32", 2e-6), ("bf16", 2e-6)])
+# fp32: the accumulation is fp32 throughout and only the order of additions changes.
+# bf16: the weights enter P.V rounded to bf16 relative to each split's own running
+# reference, so splits agree to the weights' rounding (2^-9 relative), not fp32's.
+@pytest.mark.parametrize("dtype,agree", [("f32", 2e-6), ("bf16", 4e-3)])
 def test_splits_agree_and_runs_are_deterministic(dtype, agree):
-    """Every split-K partition count gives the same result to fp32 rounding (the
-    accumulation is fp32 throughout; only the order of additions changes)."""
+    """Every split-K partition count gives the same result up to the rounding of its
+    arithmetic, and repeated runs are bitwise identical."""
     case = small_decode(seed=51, batch=4, lo=300, hi=900, W_=700, out="f32", dtype=dtype,
                         d=64 if dtype == "f32" else 128)
     dc = D.to_device(case, DEV)
