@@ -12,6 +12,7 @@ namespace qsa {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 typedef const __attribute__((address_space(1))) u32x4 global_u32x4;
 
@@ -215,9 +216,10 @@ __device__ __forceinline__ const int32_t *entry_ptr(const GatherParams &p, int64
     return jj < p.window ? dummy : p.indices + r * p.width + (jj - p.window);
 }
 
-// Stage 2 input: the position the entry names, and which leaf holds it.
+// Stage 2 input: the position the entry names, and which leaf holds it. Positions
+// are below 2^31 (int32 lists; a block-sparse position past the row is not present).
 struct KeyPos {
-    int64_t tok;       // position (or compressed entry); meaningful when present
+    int32_t tok;       // position (or compressed entry); meaningful when present
     bool comp;         // latent: compressed leaf
     bool present;
 };
@@ -228,27 +230,36 @@ __device__ __forceinline__ KeyPos key_pos(const GatherParams &p, int64_t pos, in
 {
     KeyPos k{raw, false, present};
     if constexpr (LIST == KEYS_BLOCKS) {
-        const int64_t t = jj / p.block_size;
-        k.tok = (int64_t)raw * p.block_size + (jj - t * p.block_size);
-        k.present = present && raw >= 0 && k.tok <= pos;
+        const int32_t bs = p.block_size;
+        const int32_t t = (int32_t)jj / bs;
+        const int64_t tok = (int64_t)raw * bs + ((int32_t)jj - t * bs);
+        k.present = present && raw >= 0 && tok <= pos;
+        k.tok = (int32_t)tok;
     } else if constexpr (LIST == KEYS_LATENT) {
         const bool win = jj < p.window;
-        k.tok = win ? pos - p.window + 1 + jj : raw;
+        k.tok = win ? (int32_t)(pos - p.window + 1 + jj) : raw;
         k.comp = !win;
     }
     k.present = k.present && k.tok >= 0;
     return k;
 }
 
-// Stage 2 for one leaf: logical page and slot of a position (exact below 2^31), and
-// whether the page table covers it.
-__device__ __forceinline__ const uint32_t *leaf_entry_ptr(const CacheAddr &c, int b, uint64_t t, bool &in,
+// Stage 2 for one leaf: logical page and slot of a position, and whether the page
+// table covers it (shift and mask for power-of-two page sizes, else a multiply-high
+// that is exact below 2^31).
+__device__ __forceinline__ const uint32_t *leaf_entry_ptr(const CacheAddr &c, int b, uint32_t t, bool &in,
                                                           int32_t &slot)
 {
-    const int64_t lp = (int64_t)((t * c.magic) >> c.magic_shift);
-    slot = (int32_t)(t - (uint64_t)lp * (uint64_t)c.page_size);
-    in = lp < c.max_pages;
-    return c.lut + (int64_t)b * c.max_pages + lp;
+    uint32_t lp;
+    if (c.page_shift >= 0) {
+        lp = t >> c.page_shift;
+        slot = (int32_t)(t & c.page_mask);
+    } else {
+        lp = (uint32_t)(((uint64_t)t * c.magic) >> c.magic_shift);
+        slot = (int32_t)(t - lp * (uint32_t)c.page_size);
+    }
+    in = (int64_t)lp < c.max_pages;
+    return c.lut + (uint64_t)(uint32_t)b * (uint64_t)c.max_pages + lp;
 }
 
 // Stage 2: address of the page-table entry of k (or a dummy). Updates k.present for
@@ -260,9 +271,7 @@ template <int LIST>
 __device__ __forceinline__ const uint32_t *page_entry_ptr(const GatherParams &p, int b, KeyPos &k,
                                                           int32_t &slot)
 {
-    // positions are below 2^31 (int32 lists); larger ones are outside every page table
-    k.present = k.present && k.tok < (int64_t(1) << 31);
-    const uint64_t t = (uint64_t)(k.tok & 0x7fffffff);
+    const uint32_t t = (uint32_t)k.tok & 0x7fffffffu;
     bool in;
     const uint32_t *e = leaf_entry_ptr(p.kv, b, t, in, slot);
     if constexpr (LIST == KEYS_LATENT) {
@@ -277,13 +286,14 @@ __device__ __forceinline__ const uint32_t *page_entry_ptr(const GatherParams &p,
     return k.present ? e : p.kv.lut;
 }
 
-// Stage 3 for one leaf: element offset of (page, slot) of the addressed layer.
-__device__ __forceinline__ const char *leaf_row(const CacheAddr &c, uint32_t page, int32_t slot, int64_t head,
-                                                int eb, bool &in)
+// Stage 3 for one leaf: byte address of (page, slot) of the addressed layer plus
+// `head_b` bytes: one 32x32->64 multiply-add on top of a 32-bit in-page offset.
+__device__ __forceinline__ const char *leaf_row(const CacheAddr &c, uint32_t page, int32_t slot, uint32_t head_b,
+                                                bool &in)
 {
     in = (int64_t)page < c.num_pages;
-    const int64_t off = (int64_t)page * c.page_stride + c.layer_off + (int64_t)slot * c.slot_stride + head;
-    return static_cast<const char *>(c.blocks) + off * eb;
+    const uint32_t inpage = c.layer_off_b + (uint32_t)slot * c.slot_stride_b + head_b;
+    return static_cast<const char *>(c.blocks) + ((uint64_t)page * c.page_stride_b + inpage);
 }
 
 // Stage 3: byte address of k's plane-0 row for kv head g (or `dummy`).
@@ -291,12 +301,12 @@ template <int EB, int LIST>
 __device__ __forceinline__ const char *row_address(const GatherParams &p, const KeyPos &k, uint32_t page,
                                                    int32_t slot, int g, const char *dummy, bool &present)
 {
-    const int64_t head = LIST == KEYS_LATENT ? 0 : (int64_t)g * p.head_dim;
+    const uint32_t head_b = LIST == KEYS_LATENT ? 0u : (uint32_t)(g * p.head_dim * EB);
     bool in;
-    const char *a = leaf_row(p.kv, page, slot, head, EB, in);
+    const char *a = leaf_row(p.kv, page, slot, head_b, in);
     if constexpr (LIST == KEYS_LATENT) {
         bool in_c;
-        const char *a_c = leaf_row(p.comp, page, slot, head, EB, in_c);
+        const char *a_c = leaf_row(p.comp, page, slot, head_b, in_c);
         a = k.comp ? a_c : a;
         in = k.comp ? in_c : in;
     }
@@ -317,6 +327,19 @@ __device__ __forceinline__ float final_factor(const GatherParams &p, int64_t hea
         L = L * c + __builtin_amdgcn_exp2f(sl - M2);
     }
     return L > 0.f ? c / L : 0.f;
+}
+
+// Four consecutive outputs (idx a multiple of 4): bf16 (round to nearest even) or fp32.
+__device__ __forceinline__ void store_out4(void *out, int32_t out_dtype, int64_t idx, f32x4_t v)
+{
+    if (out_dtype == QSA_BF16) {
+        typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+        const u32x2v w = {f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
+                          f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16)};
+        *reinterpret_cast<u32x2v *>(static_cast<uint16_t *>(out) + idx) = w;
+    } else {
+        *reinterpret_cast<f32x4_t *>(static_cast<float *>(out) + idx) = v;
+    }
 }
 
 // Two adjacent outputs (idx even): one 4-byte bf16 pair or one 8-byte float pair.

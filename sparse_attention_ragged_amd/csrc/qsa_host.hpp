@@ -17,6 +17,10 @@ void clear_error();
 // Addressing of one paged cache leaf, in elements. The element offset of
 // (page, plane, layer, slot, kv head, d) is
 //   page * page_stride + plane * plane_stride + layer_off + slot * slot_stride + head * D + d.
+//
+// The kernels address in bytes with 32-bit in-page offsets (a page is smaller than
+// 4 GiB, checked on the host): row = blocks + page * page_stride_b + (layer_off_b +
+// slot * slot_stride_b + head_b), one 32x32->64 multiply-add per row.
 struct CacheAddr {
     const void *blocks;
     const uint32_t *lut;
@@ -29,6 +33,12 @@ struct CacheAddr {
     int32_t page_size;
     int32_t magic_shift;    // position -> logical page: (pos * magic) >> magic_shift, exact for pos < 2^31
     uint64_t magic;
+    int32_t page_shift;     // log2(page_size) when it is a power of two, else -1
+    uint32_t page_mask;     // page_size - 1 (power of two)
+    uint32_t page_stride_b; // the strides and the layer offset in bytes
+    uint32_t plane_stride_b;
+    uint32_t layer_off_b;
+    uint32_t slot_stride_b;
 };
 
 // Key-list kinds the gather kernels walk for one (row, kv head).

@@ -1,7 +1,11 @@
 // Gather-attention on matrix cores (groups of 8 or 16 query heads per kv head).
 //
-// One workgroup owns one (query row, kv head, split); each wavefront of it walks its
-// own tiles of 32 keys of the split (the workgroup merges the wavefronts at the end).
+// Each wavefront owns one (query row, kv head, split) item and walks its keys in tiles
+// of 32, so no wavefront ever waits for or merges with another; it normalises and
+// stores its own output rows. Items are ordered kv head, row, split (split fastest), a
+// workgroup takes NW consecutive items, and workgroups are renumbered so that each of
+// the 8 XCDs walks a contiguous range of them: at any time an XCD works on neighbouring
+// rows of one kv head, whose selected keys largely coincide and stay in its L2.
 // Per tile, with gfx950 16x16x32 MFMAs (lane l: i = l % 16, q = l / 16):
 //
 //  * S^T = K . Q^T   A = 16 keys x 32 dims of K, straight from global memory (lane
@@ -22,6 +26,7 @@
 //
 // Keys reach their rows through the same three-stage address pipeline as the
 // wavefront kernel (list entry -> page-table entry -> rows), issued a tile ahead.
+// Softmax reductions over the four lanes of a head use the gfx950 row-swap permutes.
 #include <type_traits>
 
 #include "qsa_device.hpp"
@@ -31,13 +36,13 @@ namespace qsa {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef const __attribute__((address_space(1))) u32x2 global_u32x2;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 
 constexpr int kMfmaMaxWaves = 4;
+constexpr int kNumXcd = 8;            // XCDs of an MI355X; blocks are dealt to them round-robin
 constexpr int kTileKeys = 32;
 constexpr float kSlack = 8.0f;
 
@@ -74,26 +79,31 @@ __global__ void __launch_bounds__(64 * kMfmaMaxWaves) gather_mfma_kernel(GatherP
     constexpr int NC = D / 32;                  // 32-dim chunks of QK^T
     constexpr int NDT = D / 16;                 // 16-dim tiles of the output
     constexpr int VROW = D + 8;                 // LDS row of the V tile, in bf16 (+16 B)
-    constexpr int kVBytes = kMfmaMaxWaves * kTileKeys * VROW * 2;
-    constexpr int kMergeBytes = kMfmaMaxWaves * 16 * (D + 2) * 4;
-    constexpr int kSmem = kVBytes > kMergeBytes ? kVBytes : kMergeBytes;
+    constexpr int kSmem = kMfmaMaxWaves * kTileKeys * VROW * 2;   // one V tile per wavefront
     static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
     using Chunk = typename std::conditional<DT == QSA_BF16, u32x4, u32x2>::type;
     __shared__ __attribute__((aligned(16))) char smem[kSmem];
 
     const int S = p.num_splits;
-    const int Hkv = p.num_kv_heads;
     const int G = p.group;
-    int64_t bid = blockIdx.x;
-    const int g = (int)(bid % Hkv);
-    bid /= Hkv;
-    const int s = (int)(bid % S);
-    const int64_t r = bid / S;
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int NW = blockDim.x >> 6;
+
+    // XCD-contiguous renumbering of the workgroups (blocks are dealt to the 8 XCDs
+    // round-robin): XCD x takes a contiguous share of the item range
+    const int64_t nwg = gridDim.x;
+    const int64_t xq = nwg / kNumXcd, xr = nwg % kNumXcd;
+    const int64_t xcd = blockIdx.x % kNumXcd, xk = blockIdx.x / kNumXcd;
+    const int64_t wg = xcd * xq + (xcd < xr ? xcd : xr) + xk;
+    // this wavefront's item: (kv head, row, split), split fastest
+    const int64_t item = wg * NW + wave;
+    if (item >= p.total_q * (int64_t)p.num_kv_heads * S)
+        return;
+    const int s = (int)(item % S);
+    const int64_t r = (item / S) % p.total_q;
+    const int g = (int)(item / S / p.total_q);
     const int li = lane & 15;
     const int lq = lane >> 4;
     uint16_t *s_v = reinterpret_cast<uint16_t *>(smem) + wave * kTileKeys * VROW;
@@ -120,9 +130,9 @@ __global__ void __launch_bounds__(64 * kMfmaMaxWaves) gather_mfma_kernel(GatherP
         pos = (int64_t)p.cache_lengths[b] + (r - (int64_t)p.row_off[b]);
     const int64_t j0 = (int64_t)s * p.split_keys;
     const int64_t j1 = n < j0 + p.split_keys ? n : j0 + p.split_keys;
-    const int64_t per_batch = (int64_t)NW * kTileKeys;
+    const int64_t per_batch = kTileKeys;
     const int nb = j1 > j0 ? (int)((j1 - j0 + per_batch - 1) / per_batch) : 0;
-    const int64_t vdelta = LIST == KEYS_LATENT ? 0 : p.kv.plane_stride * EB;
+    const int64_t vdelta = LIST == KEYS_LATENT ? 0 : (int64_t)p.kv.plane_stride_b;
     const char *dummy = qrow0;                   // a readable row for absent keys
 
     float m = kNoKey, lsum = 0.f;                // head li (shared by the 4 lanes of li)
@@ -137,7 +147,7 @@ __global__ void __launch_bounds__(64 * kMfmaMaxWaves) gather_mfma_kernel(GatherP
 
     // this lane's two keys of tile `batch`: 16*h + li, h = 0, 1
     auto key_index = [&](int batch, int h) -> int64_t {
-        return j0 + (int64_t)batch * per_batch + (int64_t)wave * kTileKeys + 16 * h + li;
+        return j0 + (int64_t)batch * per_batch + 16 * h + li;
     };
     auto load_entries = [&](int batch, Entries &E) {
 #pragma unroll
@@ -222,8 +232,7 @@ __global__ void __launch_bounds__(64 * kMfmaMaxWaves) gather_mfma_kernel(GatherP
                 sc[h][i] = (present >> key) & 1u ? v : kNegInf;
                 mx = fmaxf(mx, sc[h][i]);
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = xor32_max(xor16_max(mx));
         if (__any(mx > m + kSlack)) {
             const float alpha = __builtin_amdgcn_exp2f(m - mx);
             lsum *= alpha;
@@ -288,45 +297,25 @@ __global__ void __launch_bounds__(64 * kMfmaMaxWaves) gather_mfma_kernel(GatherP
         }
     }
 
-    // per-head state of this wavefront: sum the four lanes of each head
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-
-    // merge the wavefronts through LDS: s_ml [NW][16][2], s_acc [NW][16][D]
-    __syncthreads();
-    float *s_ml = reinterpret_cast<float *>(smem);
-    float *s_acc = s_ml + kMfmaMaxWaves * 16 * 2;
-    if (lq == 0) {
-        s_ml[(wave * 16 + li) * 2] = m;
-        s_ml[(wave * 16 + li) * 2 + 1] = lsum;
-    }
-#pragma unroll
-    for (int t = 0; t < NDT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            s_acc[(wave * 16 + li) * D + 16 * t + 4 * lq + i] = acc[t][i];
-    __syncthreads();
-    for (int idx = tid; idx < G * D; idx += blockDim.x) {
-        const int h = idx / D;
-        const int d = idx - h * D;
-        float M = kNoKey;
-        for (int w = 0; w < NW; ++w)
-            M = fmaxf(M, s_ml[(w * 16 + h) * 2]);
-        float L = 0.f, A = 0.f;
-        for (int w = 0; w < NW; ++w) {
-            const float c = __builtin_amdgcn_exp2f(s_ml[(w * 16 + h) * 2] - M);
-            L += c * s_ml[(w * 16 + h) * 2 + 1];
-            A += c * s_acc[(w * 16 + h) * D + d];
-        }
-        const int64_t rh = r * p.num_q_heads + (int64_t)g * G + h;
+    // per-head sum over the four lanes of each head; lane (i, q) then stores dims
+    // 16t + 4q .. 16t + 4q + 3 of head i
+    lsum = xor32_sum(xor16_sum(lsum));
+    if (li < G) {
+        const int64_t head = (int64_t)g * G + li;
+        const int64_t rh = r * p.num_q_heads + head;
         if (S == 1) {
-            store_out(p.out, p.out_dtype, rh * D + d, A * final_factor(p, (int64_t)g * G + h, M, L));
+            const float f = final_factor(p, head, m, lsum);
+#pragma unroll
+            for (int t = 0; t < NDT; ++t)
+                store_out4(p.out, p.out_dtype, rh * D + 16 * t + 4 * lq, acc[t] * f);
         } else {
             const int64_t srh = (int64_t)s * p.total_q * p.num_q_heads + rh;
-            p.ws_acc[srh * D + d] = A;
-            if (d == 0) {
-                p.ws_ml[srh * 2] = M;
-                p.ws_ml[srh * 2 + 1] = L;
+#pragma unroll
+            for (int t = 0; t < NDT; ++t)
+                *reinterpret_cast<f32x4_t *>(p.ws_acc + srh * D + 16 * t + 4 * lq) = acc[t];
+            if (lq == 0) {
+                p.ws_ml[srh * 2] = m;
+                p.ws_ml[srh * 2 + 1] = lsum;
             }
         }
     }
@@ -335,12 +324,13 @@ __global__ void __launch_bounds__(64 * kMfmaMaxWaves) gather_mfma_kernel(GatherP
 template <int DT, int D, int LIST>
 int launch_mfma(const GatherParams &p, void *stream)
 {
-    const int64_t grid = p.total_q * (int64_t)p.num_kv_heads * p.num_splits;
+    const int waves = p.waves < kMfmaMaxWaves ? p.waves : kMfmaMaxWaves;
+    const int64_t items = p.total_q * (int64_t)p.num_kv_heads * p.num_splits;
+    const int64_t grid = (items + waves - 1) / waves;
     if (grid <= 0)
         return 0;
     if (grid > 0x7fffffff)
         return (int)hipErrorInvalidConfiguration;
-    const int waves = p.waves < kMfmaMaxWaves ? p.waves : kMfmaMaxWaves;
     hipLaunchKernelGGL((gather_mfma_kernel<DT, D, LIST>), dim3((unsigned)grid), dim3(64 * waves), 0,
                        static_cast<hipStream_t>(stream), p);
     return (int)hipGetLastError();

@@ -33,7 +33,6 @@ namespace qsa {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 
@@ -55,19 +54,6 @@ __device__ __forceinline__ bf16x8_t wide_bf16x8(u32x4 v)
 
 // Workgroup barrier that orders LDS accesses only: global loads stay in flight.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Four consecutive outputs of one head: bf16 (round to nearest even) or fp32.
-__device__ __forceinline__ void store_out4(void *out, int32_t out_dtype, int64_t idx, f32x4_t v)
-{
-    if (out_dtype == QSA_BF16) {
-        typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
-        const u32x2v w = {f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
-                          f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16)};
-        *reinterpret_cast<u32x2v *>(static_cast<uint16_t *>(out) + idx) = w;
-    } else {
-        *reinterpret_cast<f32x4_t *>(static_cast<float *>(out) + idx) = v;
-    }
-}
 
 template <int D>
 __global__ void __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))

@@ -72,6 +72,10 @@ qsa_status check_cache(const qsa_paged_cache *c, const char *what, int64_t plane
     if (!aligned16(c->blocks) || (c->head_dim * eb) % 16 != 0 || (stride * eb) % 16 != 0)
         return fail(QSA_ERR_SHAPE, "%s: blocks, head_dim rows and page_stride must keep 16-byte "
                                    "alignment", what);
+    // in-page offsets and the page stride are 32-bit byte quantities in the kernels
+    if (stride * eb >= (int64_t(1) << 32))
+        return fail(QSA_ERR_UNSUPPORTED, "%s: pages of 4 GiB or more (page_stride %lld elements) are not "
+                                         "supported", what, (long long)stride);
     return QSA_OK;
 }
 
@@ -162,7 +166,10 @@ qsa_status plan_gather(const qsa_ragged_q *q, int64_t num_kv_heads, int32_t dtyp
     const int64_t items = q->total_q * (num_kv_heads / plan->head_block);
     int64_t splits = o.num_splits;
     if (splits == 0) {
-        splits = items > 0 ? ceil_div(kTargetWorkgroups, items) : 1;
+        // the matrix-core kernel gives each wavefront its own (row, kv head, split)
+        const int64_t target = plan->path == PATH_MFMA ? kTargetWorkgroups * (plan->waves < 4 ? plan->waves : 4)
+                                                       : kTargetWorkgroups;
+        splits = items > 0 ? ceil_div(target, items) : 1;
         int64_t by_len = ceil_div(cap, kMinKeysPerSplit);
         if (splits > by_len)
             splits = by_len;
@@ -212,6 +219,14 @@ CacheAddr cache_addr(const qsa_paged_cache *c, uint32_t layer)
     const unsigned __int128 num = (unsigned __int128)1 << (31 + k);
     a.magic = (uint64_t)((num + (unsigned __int128)c->page_size - 1) / (unsigned __int128)c->page_size);
     a.magic_shift = 31 + k;
+    const bool pow2 = (c->page_size & (c->page_size - 1)) == 0;
+    a.page_shift = pow2 ? k : -1;
+    a.page_mask = pow2 ? (uint32_t)(c->page_size - 1) : 0u;
+    const int64_t eb = elem_bytes(c->dtype);
+    a.page_stride_b = (uint32_t)(a.page_stride * eb);   // < 2^32: checked in check_cache
+    a.plane_stride_b = (uint32_t)(a.plane_stride * eb);
+    a.layer_off_b = (uint32_t)(a.layer_off * eb);
+    a.slot_stride_b = (uint32_t)(a.slot_stride * eb);
     return a;
 }
 

@@ -55,7 +55,6 @@ template <int DT, int D, int G, int U, int LIST>
 __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParams p)
 {
     constexpr int EB = Elem<DT>::bytes;
-    constexpr int ROWB = D * EB;                 // bytes of one K (or V) row
     constexpr int EPC = 16 / EB;                 // elements per chunk
     // 16-byte chunks per lane: two where a lane then holds at most 16 elements (bf16,
     // fp32); e4m3 keeps one (its q is widened to fp32 in registers)
@@ -109,7 +108,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParam
     const int64_t j1 = n < j0 + p.split_keys ? n : j0 + p.split_keys;
     const int64_t per_batch = (int64_t)NK * U;
     const int nb = j1 > j0 ? (int)((j1 - j0 + per_batch - 1) / per_batch) : 0;
-    const int64_t vdelta = LIST == KEYS_LATENT ? 0 : p.kv.plane_stride * EB;
+    const int64_t vdelta = LIST == KEYS_LATENT ? 0 : (int64_t)p.kv.plane_stride_b;
     const char *dummy = qbase;                   // a readable row for absent keys
 
     float qf[G][DT == QSA_BF16 ? 1 : EPL];
