@@ -8,10 +8,17 @@
 // rows of one kv head, whose selected keys largely coincide and stay in its L2.
 // Per tile, with gfx950 16x16x32 MFMAs (lane l: i = l % 16, q = l / 16):
 //
-//  * S^T = K . Q^T   A = 16 keys x 32 dims of K, straight from global memory (lane
-//                    holds 8 consecutive dims of key i), B = Q^T (8 dims of head i,
-//                    loaded once). Two key halves x head_dim/32 chunks of MFMAs; C
-//                    holds, per lane, keys 4q..4q+3 (+16) of head i.
+//  * loads          lane l walks key l % 32 of the tile through the address pipeline;
+//                    the K and V rows are then loaded row-contiguous (one load
+//                    instruction covers whole rows, 16 bytes a lane, each lane taking
+//                    its row's address from the lane that computed it) and written to
+//                    the wavefront's own LDS tiles. (Loading straight into the MFMA
+//                    fragment layout touches 16 rows x 64 bytes per instruction and
+//                    measured at well under half the L2 gather rate.)
+//  * S^T = K . Q^T   A = 16 keys x 32 dims of K from the LDS tile (lane holds 8
+//                    consecutive dims of key i), B = Q^T (8 dims of head i, loaded
+//                    once). Two key halves x head_dim/32 chunks of MFMAs; C holds, per
+//                    lane, keys 4q..4q+3 (+16) of head i.
 //  * softmax         per head i, over the four lanes sharing i, in the log2 domain
 //                    with the same lazy rescale as the wavefront kernel.
 //  * O^T += V^T P^T  B = P^T comes straight out of the S^T accumulator layout (the
@@ -73,16 +80,22 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 w)
 }
 
 template <int DT, int D, int LIST>
-__global__ void __launch_bounds__(64 * kMfmaMaxWaves) gather_mfma_kernel(GatherParams p)
+__global__ void __launch_bounds__(64 * kMfmaMaxWaves) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
+gather_mfma_kernel(GatherParams p)
 {
     constexpr int EB = Elem<DT>::bytes;
     constexpr int NC = D / 32;                  // 32-dim chunks of QK^T
     constexpr int NDT = D / 16;                 // 16-dim tiles of the output
-    constexpr int VROW = D + 8;                 // LDS row of the V tile, in bf16 (+16 B)
-    constexpr int kSmem = kMfmaMaxWaves * kTileKeys * VROW * 2;   // one V tile per wavefront
-    static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
+    constexpr int RB = D * EB;                  // bytes of one K (or V) row in the cache
+    constexpr int LPK = RB / 16;                // lanes that load one row (16 bytes each)
+    constexpr int KPI = 64 / LPK;               // rows per load instruction
+    constexpr int NI = kTileKeys / KPI;         // load instructions per plane and tile
+    constexpr int KROWB = RB + 32;              // LDS row of the K tile (bytes), padded
+    constexpr int VROW = D + 16;                // LDS row of the V tile (bf16 elements), padded
+    constexpr int kWaveLds = kTileKeys * (KROWB + 2 * VROW);
+    static_assert(D % 32 == 0 && LPK >= 1 && LPK <= 64 && kTileKeys % KPI == 0, "unsupported head_dim");
     using Chunk = typename std::conditional<DT == QSA_BF16, u32x4, u32x2>::type;
-    __shared__ __attribute__((aligned(16))) char smem[kSmem];
+    __shared__ __attribute__((aligned(16))) char smem[kMfmaMaxWaves * kWaveLds];
 
     const int S = p.num_splits;
     const int G = p.group;
@@ -104,9 +117,11 @@ __global__ void __launch_bounds__(64 * kMfmaMaxWaves) gather_mfma_kernel(GatherP
     const int s = (int)(item % S);
     const int64_t r = (item / S) % p.total_q;
     const int g = (int)(item / S / p.total_q);
+
     const int li = lane & 15;
     const int lq = lane >> 4;
-    uint16_t *s_v = reinterpret_cast<uint16_t *>(smem) + wave * kTileKeys * VROW;
+    char *s_k = smem + wave * kWaveLds;                                     // [32][KROWB] bytes
+    uint16_t *s_v = reinterpret_cast<uint16_t *>(s_k + kTileKeys * KROWB);   // [32][VROW] bf16
 
     // prologue: list length, sequence and the q fragments go out together
     const int64_t n = key_list_length(p, r);
@@ -130,8 +145,7 @@ __global__ void __launch_bounds__(64 * kMfmaMaxWaves) gather_mfma_kernel(GatherP
         pos = (int64_t)p.cache_lengths[b] + (r - (int64_t)p.row_off[b]);
     const int64_t j0 = (int64_t)s * p.split_keys;
     const int64_t j1 = n < j0 + p.split_keys ? n : j0 + p.split_keys;
-    const int64_t per_batch = kTileKeys;
-    const int nb = j1 > j0 ? (int)((j1 - j0 + per_batch - 1) / per_batch) : 0;
+    const int nb = j1 > j0 ? (int)((j1 - j0 + kTileKeys - 1) / kTileKeys) : 0;
     const int64_t vdelta = LIST == KEYS_LATENT ? 0 : (int64_t)p.kv.plane_stride_b;
     const char *dummy = qrow0;                   // a readable row for absent keys
 
@@ -141,85 +155,79 @@ __global__ void __launch_bounds__(64 * kMfmaMaxWaves) gather_mfma_kernel(GatherP
     for (int t = 0; t < NDT; ++t)
         acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    struct Entries { int32_t raw[2]; };
-    struct Pages { KeyPos k[2]; int32_t slot[2]; uint32_t page[2]; };
-    struct Rows { Chunk k[2][NC], v[2][NC]; bool ok[2]; };
+    // Lane l (and l + 32) walks key l % 32 of each tile through the address pipeline;
+    // the rows are then loaded row-contiguous: load instruction i of a plane reads rows
+    // i*KPI .. i*KPI + KPI-1, LPK lanes per row, and every lane fetches its row's
+    // address from the lane that computed it.
+    const int kl = lane & 31;
+    const int my_row = lane / LPK;              // row within a load instruction
+    const int my_chunk = lane % LPK;            // 16-byte chunk within the row
+    struct Entries { int32_t raw; };
+    struct Pages { KeyPos k; int32_t slot; uint32_t page; };
+    struct Rows { u32x4 k[NI], v[NI]; uint32_t present; };
 
-    // this lane's two keys of tile `batch`: 16*h + li, h = 0, 1
-    auto key_index = [&](int batch, int h) -> int64_t {
-        return j0 + (int64_t)batch * per_batch + 16 * h + li;
-    };
+    auto key_index = [&](int batch) -> int64_t { return j0 + (int64_t)batch * kTileKeys + kl; };
     auto load_entries = [&](int batch, Entries &E) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int64_t jj = key_index(batch, h);
-            E.raw[h] = *entry_ptr<LIST>(p, r, g, jj, jj < j1);
-        }
+        const int64_t jj = key_index(batch);
+        E.raw = *entry_ptr<LIST>(p, r, g, jj, jj < j1);
     };
     auto load_pages = [&](int batch, const Entries &E, Pages &P) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int64_t jj = key_index(batch, h);
-            P.k[h] = key_pos<LIST>(p, pos, jj, E.raw[h], jj < j1);
-            P.page[h] = *page_entry_ptr<LIST>(p, b, P.k[h], P.slot[h]);
-        }
+        const int64_t jj = key_index(batch);
+        P.k = key_pos<LIST>(p, pos, jj, E.raw, jj < j1);
+        P.page = *page_entry_ptr<LIST>(p, b, P.k, P.slot);
     };
     auto load_rows = [&](const Pages &P, Rows &R) {
+        bool ok;
+        const char *a = row_address<EB, LIST>(p, P.k, P.page, P.slot, g, dummy, ok);
+        R.present = (uint32_t)(__ballot(ok) & 0xffffffffull);
+        const char *own = ok ? a : dummy;
+        const uint32_t lo = (uint32_t)(uintptr_t)own, hi = (uint32_t)((uintptr_t)own >> 32);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            bool ok;
-            const char *a = row_address<EB, LIST>(p, P.k[h], P.page[h], P.slot[h], g, dummy, ok);
-            R.ok[h] = ok;
-            const char *ka = ok ? a : dummy;
-            const char *va = ok ? a + vdelta : dummy;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                if constexpr (DT == QSA_BF16) {
-                    R.k[h][c] = ldg16(ka + (32 * c + 8 * lq) * EB);
-                    R.v[h][c] = ldg16(va + (32 * c + 8 * lq) * EB);
-                } else {
-                    R.k[h][c] = ldg8(ka + (32 * c + 8 * lq) * EB);
-                    R.v[h][c] = ldg8(va + (32 * c + 8 * lq) * EB);
-                }
-            }
+        for (int i = 0; i < NI; ++i) {
+            const int src = i * KPI + my_row;
+            const uintptr_t ra = ((uintptr_t)(uint32_t)__shfl((int)hi, src) << 32) | (uint32_t)__shfl((int)lo, src);
+            const bool rok = (R.present >> src) & 1u;
+            const char *kaddr = reinterpret_cast<const char *>(ra) + my_chunk * 16;
+            R.k[i] = ldg16(kaddr);
+            R.v[i] = ldg16(rok ? kaddr + vdelta : dummy + my_chunk * 16);
         }
     };
     auto consume = [&](const Rows &R) {
-        // key-presence mask of the tile: bit k = key 16*h + k%16 present
-        const uint32_t m0 = (uint32_t)(__ballot(R.ok[0]) & 0xffffu);
-        const uint32_t m1 = (uint32_t)(__ballot(R.ok[1]) & 0xffffu);
-        const uint32_t present = m0 | (m1 << 16);
-        // S^T (two 16-key halves)
+        const uint32_t present = R.present;
+        // rows -> the wavefront's LDS tiles (V widened to bf16); LDS operations of one
+        // wavefront execute in order, the empty asm statements keep the compiler from
+        // moving the accesses across each other
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int row = i * KPI + my_row;
+            *reinterpret_cast<u32x4 *>(s_k + row * KROWB + my_chunk * 16) = R.k[i];
+            if constexpr (DT == QSA_BF16) {
+                *reinterpret_cast<u32x4 *>(s_v + row * VROW + my_chunk * 8) = R.v[i];
+            } else {
+                *reinterpret_cast<u32x4 *>(s_v + row * VROW + my_chunk * 16) =
+                    e4m3x8_to_bf16x8(u32x2{R.v[i][0], R.v[i][1]});
+                *reinterpret_cast<u32x4 *>(s_v + row * VROW + my_chunk * 16 + 8) =
+                    e4m3x8_to_bf16x8(u32x2{R.v[i][2], R.v[i][3]});
+            }
+        }
+        asm volatile("" ::: "memory");
+        // S^T (two 16-key halves); A = 8 dims of key 16h + i from the K tile
         f32x4_t st[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             st[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
+                const char *kp = s_k + (16 * h + li) * KROWB + (32 * c + 8 * lq) * EB;
                 if constexpr (DT == QSA_BF16)
-                    st[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k[h][c]), as_bf16x8(qf[c]),
-                                                                    st[h], 0, 0, 0);
+                    st[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(*reinterpret_cast<const u32x4 *>(kp)),
+                                                                    as_bf16x8(qf[c]), st[h], 0, 0, 0);
                 else
-                    st[h] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(R.k[h][c]), as_long(qf[c]), st[h],
-                                                                          0, 0, 0);
+                    st[h] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+                        as_long(*reinterpret_cast<const u32x2 *>(kp)), as_long(qf[c]), st[h], 0, 0, 0);
             }
         }
-        // V tile -> LDS (bf16 rows); read back transposed below by this wavefront only.
-        // LDS operations of one wavefront execute in order; the empty asm statements
-        // keep the compiler from moving the accesses across each other.
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                u32x4 v;
-                if constexpr (DT == QSA_BF16)
-                    v = R.v[h][c];
-                else
-                    v = e4m3x8_to_bf16x8(R.v[h][c]);
-                *reinterpret_cast<u32x4 *>(s_v + (16 * h + li) * VROW + 32 * c + 8 * lq) = v;
-            }
-        asm volatile("" ::: "memory");
         // scores in the log2 domain, absent keys at -inf
         float sc[2][4];
         float mx = m;
@@ -267,6 +275,7 @@ __global__ void __launch_bounds__(64 * kMfmaMaxWaves) gather_mfma_kernel(GatherP
             __builtin_memcpy(reinterpret_cast<char *>(&av) + 8, &a1, 8);
             acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(pb), acc[t], 0, 0, 0);
         }
+        asm volatile("" ::: "memory");
     };
 
     if (nb > 0) {
