@@ -65,10 +65,14 @@ class _Ragged(ctypes.Structure):
                 ("reserved1", ctypes.c_uint32)]
 
 
+SCHEDULE_CODE = {"auto": 0, "static": 1, "dynamic": 2}
+
+
 class LaunchOptions(ctypes.Structure):
-    """Launch knobs: split-K partitions, wavefronts per workgroup, keys in flight (0 = auto)."""
+    """Launch knobs: split-K partitions, wavefronts per workgroup, keys in flight (0 = auto)
+    and the work schedule (0 auto, 1 static, 2 dynamic)."""
     _fields_ = [("num_splits", ctypes.c_int32), ("waves", ctypes.c_int32),
-                ("unroll", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("unroll", ctypes.c_int32), ("schedule", ctypes.c_int32)]
 
 
 def _load():
@@ -170,7 +174,9 @@ def _opts(options):
         return None
     if isinstance(options, LaunchOptions):
         return ctypes.byref(options)
-    o = LaunchOptions(options.get("num_splits", 0), options.get("waves", 0), options.get("unroll", 0), 0)
+    sched = options.get("schedule", 0)
+    sched = SCHEDULE_CODE[sched] if isinstance(sched, str) else int(sched)
+    o = LaunchOptions(options.get("num_splits", 0), options.get("waves", 0), options.get("unroll", 0), sched)
     return ctypes.byref(o)
 
 
@@ -184,7 +190,9 @@ def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
     if nbytes == 0:
         return None, 0
     if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        # zero-filled: the dynamic schedule's work counter must start at zero (every
+        # call leaves it zero, so a workspace passed back in needs no refill)
+        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
     elif workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError("workspace too small: %d bytes needed" % nbytes)
     return workspace, workspace.numel() * workspace.element_size()

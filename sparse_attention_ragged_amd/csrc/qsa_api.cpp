@@ -39,9 +39,14 @@ void fill_common(GatherParams &p, void *out, int32_t out_dtype, const qsa_ragged
     p.unroll = plan.unroll;
     p.split_keys = plan.split_keys;
     p.head_block = plan.head_block;
-    if (plan.num_splits > 1) {
+    if (plan.num_splits > 1 || plan.schedule == SCHED_DYNAMIC) {
         p.ws_acc = static_cast<float *>(ws);
         p.ws_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + plan.ws_ml_offset);
+    }
+    if (plan.schedule == SCHED_DYNAMIC) {
+        p.sched_counter = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + plan.ws_ctr_offset);
+        p.sched_bpu = plan.sched_bpu;
+        p.sched_grid = plan.sched_grid;
     }
 }
 
@@ -52,13 +57,16 @@ qsa_status run(const GatherParams &p, const Plan &plan, void *stream)
     int err = 0;
     if (t_ev_start && t_ev_stop)
         err = record_event(t_ev_start, stream);
+    const bool dyn = plan.schedule == SCHED_DYNAMIC;
     if (!err)
-        err = plan.path == PATH_MFMA_WIDE ? launch_gather_mfma_wide(p, stream)
-              : plan.path == PATH_MFMA  ? launch_gather_mfma(p, stream)
-                                        : launch_gather_valu(p, stream);
+        err = dyn                          ? launch_gather_valu_dyn(p, stream)
+              : plan.path == PATH_MFMA_WIDE ? launch_gather_mfma_wide(p, stream)
+              : plan.path == PATH_MFMA      ? launch_gather_mfma(p, stream)
+                                            : launch_gather_valu(p, stream);
     if (!err && t_ev_start && t_ev_stop)
         err = record_event(t_ev_stop, stream);
-    if (!err && plan.num_splits > 1)
+    // the combine step also returns the dynamic schedule's counter to zero
+    if (!err && (plan.num_splits > 1 || dyn))
         err = launch_splitk_combine(p, stream);
     if (err)
         return fail(QSA_ERR_HIP, "HIP launch failed: %s", hip_error_text(err));

@@ -158,23 +158,64 @@ __device__ __forceinline__ int find_seq(const uint32_t *row_off, int batch, uint
     return lo;
 }
 
-// Sequence of row r, found by the whole wavefront at once: lane t tests sequence
-// base + t, so up to 64 sequences cost one memory round trip. Rows past the last
-// offset belong to the last sequence.
-__device__ __forceinline__ int find_seq_wave(const uint32_t *row_off, int batch, uint32_t r)
+// Sequence of row r and the row's position (cache_lengths[b] + r - row_off[b]) in one
+// memory round trip: lane t also loads cache_lengths[base + t] next to the offsets.
+// `pos` is left at 0 when cache_lengths is null.
+__device__ __forceinline__ int find_seq_pos_wave(const uint32_t *row_off, const uint32_t *cache_lengths, int batch,
+                                                 uint32_t r, int64_t &pos)
 {
-    if (batch > 1024)
-        return find_seq(row_off, batch, r);
+    if (batch > 1024) {
+        const int b = find_seq(row_off, batch, r);
+        pos = cache_lengths ? (int64_t)cache_lengths[b] + ((int64_t)r - (int64_t)row_off[b]) : 0;
+        return b;
+    }
     const int lane = threadIdx.x & 63;
     for (int base = 0; base < batch; base += 64) {
         const int t = base + lane;
         const uint32_t lo = t < batch ? row_off[t] : 0xffffffffu;
         const uint32_t hi = t < batch ? row_off[t + 1] : 0u;
+        const uint32_t cl = cache_lengths && t < batch ? cache_lengths[t] : 0u;
         const unsigned long long m = __ballot(lo <= r && r < hi);
-        if (m)
-            return base + __ffsll((long long)m) - 1;
+        if (m) {
+            const int w = __ffsll((long long)m) - 1;
+            pos = (int64_t)(uint32_t)__shfl((int)cl, w) + ((int64_t)r - (int64_t)(uint32_t)__shfl((int)lo, w));
+            return base + w;
+        }
     }
+    // rows past the last offset belong to the last sequence
+    pos = cache_lengths ? (int64_t)cache_lengths[batch - 1] + ((int64_t)r - (int64_t)row_off[batch - 1]) : 0;
     return batch - 1;
+}
+
+// Barrier that waits only for this wavefront's LDS operations (__syncthreads also
+// drains every vector-memory load in flight, which stalls a load pipeline).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// A zero the compiler cannot see through, held in a vector register: an address that
+// adds it is taken as per-lane, so the load goes through the vector memory path.
+__device__ __forceinline__ int32_t opaque_vzero()
+{
+    int32_t z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    return z;
+}
+
+// Number of keys in the list of row r (before splitting), as a per-lane value. For
+// token-index lists counts[r] is read with a vector load: a scalar load would be
+// waited for together with every later kernel-argument load (scalar loads complete
+// out of order, so every such wait is a wait for all of them); as a vector load it
+// completes in order with the loads issued after it.
+template <int LIST>
+__device__ __forceinline__ int64_t key_list_length_v(const GatherParams &p, int64_t r)
+{
+    if constexpr (LIST == KEYS_TOKEN_INDICES) {
+        const int64_t n = p.counts[r + opaque_vzero()];
+        return n < 0 ? 0 : (n > p.width ? p.width : n);
+    } else if constexpr (LIST == KEYS_BLOCKS) {
+        return p.width * p.block_size;
+    } else {
+        return p.window + p.width;
+    }
 }
 
 // Number of keys in the list of row r (before splitting).

@@ -52,8 +52,6 @@ __device__ __forceinline__ bf16x8_t wide_bf16x8(u32x4 v)
     return r;
 }
 
-// Workgroup barrier that orders LDS accesses only: global loads stay in flight.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int D>
 __global__ void __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -137,8 +135,8 @@ gather_mfma_wide_kernel(GatherParams p)
         return;
     }
     {
-        const int b = find_seq_wave(p.row_off, p.batch, (uint32_t)r);
-        const int64_t pos = (int64_t)p.cache_lengths[b] + (r - (int64_t)p.row_off[b]);
+        int b = 0;          // sequence and position: found after the first list entries left
+        int64_t pos = 0;
         const char *dummy = qrow0;
         const int skey = tid / TPK;
         const int ssub = tid % TPK;
@@ -304,6 +302,7 @@ gather_mfma_wide_kernel(GatherParams p)
 #pragma unroll
         for (int j = 0; j <= 3 * kDepth; ++j)
             e_fill[j] = load_entry(j);
+        b = find_seq_pos_wave(p.row_off, p.cache_lengths, p.batch, (uint32_t)r, pos);
         Page p_fill[2 * kDepth + 1];
 #pragma unroll
         for (int j = 0; j <= 2 * kDepth; ++j)

@@ -1,17 +1,13 @@
 // Gather-attention kernel on wavefront dot products (groups of 1, 2 or 4 query
-// heads per kv head).
+// heads per kv head), statically scheduled.
 //
 // One workgroup owns one (query row, kv head, split) and walks that split of the
 // row's key list ("QSASparseAttentionRaggedPaged": token_indices up to counts;
 // "Struct_msa_attention_ragged_paged": the positions of the listed blocks up to the
 // row's position; "latent_sparse_attention_ragged_paged": window positions, then
-// listed compressed entries).
+// listed compressed entries). The per-team scoring, softmax fold and team merge are
+// the shared core of qsa_valu_core.hpp.
 //
-//  * Teams: a team of TL lanes owns one (key, kv head) at a time; each lane holds CPL
-//    16-byte chunks of the K row and of the V row (chunk c of lane l is chunk c*TL + l
-//    of the row, so one load instruction reads TL consecutive chunks). Two chunks per
-//    lane (bf16, fp32) halve the per-key address arithmetic and shorten the team
-//    reduction.
 //  * Head blocks: when all kv heads read the same keys (token-index and latent
 //    lists), a workgroup covers a block of HB kv heads and the teams of a wavefront
 //    are HB heads x (64/TL/HB) key slots. At HB = 8 (bf16, head_dim 128, 8 kv heads) a
@@ -26,54 +22,39 @@
 //    waits for exactly the oldest batch. There is no staging phase and no barrier
 //    before the first K/V load: a workgroup reaches full speed after three memory
 //    latencies.
-//  * Scores: per head, a lane's partial dot product (packed bf16 dot instruction on
-//    the raw q and K words; fp32 FMAs otherwise) is summed over the team with DPP,
-//    scaled into the log2 domain, and folded into a running (reference, sum, acc)
-//    state in fp32. The reference only moves when a score exceeds it by more than
-//    2^8 (then the whole wavefront rescales), so most batches skip the rescale.
-//  * P.V for bf16: the weights of two keys are rounded to bf16 and paired, the two
-//    keys' V elements are paired with byte permutes, and one packed bf16 dot
-//    instruction adds both products in fp32; the running sum adds the same rounded
-//    weights, so numerator and denominator use identical weights. fp32 and e4m3 use
-//    fp32 FMAs on the widened values.
 //  * Merge: teams of a wavefront merge with lane shuffles, wavefronts through LDS;
 //    the result is the normalised output row (one split) or an (m, l, acc) partial
 //    for the split-K combine kernel.
 #include <atomic>
 #include <type_traits>
 
-#include "qsa_device.hpp"
+#include "qsa_valu_core.hpp"
 
 namespace qsa {
 
 namespace {
 
 constexpr int kMaxWaves = 8;
-constexpr float kRescaleSlack = 8.0f;   // log2 units: weights stay <= 2^8
 
 template <int DT, int D, int G, int U, int LIST>
 __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParams p)
 {
-    constexpr int EB = Elem<DT>::bytes;
-    constexpr int EPC = 16 / EB;                 // elements per chunk
-    // 16-byte chunks per lane: two where a lane then holds at most 16 elements (bf16,
-    // fp32); e4m3 keeps one (its q is widened to fp32 in registers)
-    constexpr int CPL = valu_chunks_per_lane(EB, D);
-    constexpr int TL = valu_team_lanes(EB, D);   // lanes per team
-    constexpr int TPW = 64 / TL;                 // teams per wavefront
-    constexpr int EPL = EPC * CPL;               // elements per lane
-    constexpr bool kPaired = DT == QSA_BF16 && U % 2 == 0;
-    static_assert(TL >= 1 && TL <= 64 && 64 % TL == 0, "unsupported head_dim for this dtype");
+    using Core = ValuCore<DT, D, G, U>;
+    constexpr int EB = Core::EB;
+    constexpr int EPC = Core::EPC;
+    constexpr int CPL = Core::CPL;
+    constexpr int TL = Core::TL;
+    constexpr int TPW = Core::TPW;
     extern __shared__ __attribute__((aligned(16))) float smem[];   // [NW][HB*G][2], then [NW][HB*G][D]
 
     const int S = p.num_splits;
     const int HB = p.head_block;                 // kv heads of this workgroup, one team each
-    int64_t bid = blockIdx.x;
-    const int nhb = p.num_kv_heads / HB;
+    uint32_t bid = blockIdx.x;                   // grid < 2^31 (checked by the launcher)
+    const uint32_t nhb = (uint32_t)(p.num_kv_heads / HB);
     const int gb = (int)(bid % nhb);
     bid /= nhb;
-    const int s = (int)(bid % S);
-    const int64_t r = bid / S;
+    const int s = (int)(bid % (uint32_t)S);
+    const int64_t r = bid / (uint32_t)S;
 
     const int tid = threadIdx.x;
     const int nthreads = blockDim.x;
@@ -88,58 +69,33 @@ __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParam
     const int g = gb * HB + hh;
     const int NK = NW * KPW;                     // key slots per workgroup
 
-    // element offset of chunk c of this lane within a row
-    auto chunk_elem = [&](int c) { return (c * TL + ln) * EPC; };
-
-    // prologue: list length, sequence and the q rows go out together
-    const int64_t n = key_list_length(p, r);
+    // prologue: list length and the q rows go out together
+    const int64_t n = key_list_length_v<LIST>(p, r);
     const char *qbase = static_cast<const char *>(p.q) + ((r * p.num_q_heads + (int64_t)g * G) * D) * EB;
-    u32x4 qraw[G][CPL];
+    typename Core::Q q;
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int c = 0; c < CPL; ++c)
-            qraw[h][c] = ldg16(qbase + ((int64_t)h * D + chunk_elem(c)) * EB);
-    const int b = find_seq_wave(p.row_off, p.batch, (uint32_t)r);
+            q.raw[h][c] = ldg16(qbase + ((int64_t)h * D + Core::chunk_elem(c, ln)) * EB);
+    int b = 0;              // sequence and position: found after the first list entries left
     int64_t pos = 0;
-    if constexpr (LIST != KEYS_TOKEN_INDICES)
-        pos = (int64_t)p.cache_lengths[b] + (r - (int64_t)p.row_off[b]);
     const int64_t j0 = (int64_t)s * p.split_keys;
-    const int64_t j1 = n < j0 + p.split_keys ? n : j0 + p.split_keys;
+    const int64_t jend = j0 + p.split_keys;
+    const int64_t j1 = n < jend ? n : jend;
     const int64_t per_batch = (int64_t)NK * U;
     const int nb = j1 > j0 ? (int)((j1 - j0 + per_batch - 1) / per_batch) : 0;
     const int64_t vdelta = LIST == KEYS_LATENT ? 0 : (int64_t)p.kv.plane_stride_b;
     const char *dummy = qbase;                   // a readable row for absent keys
 
-    float qf[G][DT == QSA_BF16 ? 1 : EPL];
-    if constexpr (DT != QSA_BF16) {
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int c = 0; c < CPL; ++c)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if constexpr (DT == QSA_F32)
-                        qf[h][c * EPC + i] = __uint_as_float(qraw[h][c][i]);
-                    else
-                        e4m3x4_to_f32(qraw[h][c][i], &qf[h][c * EPC + 4 * i]);
-                }
-    }
-
-    float m[G], l[G], acc[G][EPL];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        m[h] = kNoKey;
-        l[h] = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e)
-            acc[h][e] = 0.f;
-    }
+    Core::widen_q(q);
+    Core st;
+    st.reset();
 
     // ---- pipeline stages (each issues exactly one load per key on every path)
     struct Entries { int32_t raw[U]; };
     struct Pages { KeyPos k[U]; int32_t slot[U]; uint32_t page[U]; };
-    struct Rows { u32x4 k[U][CPL], v[U][CPL]; bool ok[U]; };
+    using Rows = typename Core::Rows;
 
     auto key_index = [&](int batch, int u) -> int64_t {
         return j0 + batch * per_batch + u * NK + wave * KPW + ks;
@@ -168,126 +124,13 @@ __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParam
             const char *base = ok ? a : dummy;
 #pragma unroll
             for (int c = 0; c < CPL; ++c)
-                R.k[u][c] = ldg16(base + (int64_t)chunk_elem(c) * EB);
+                R.k[u][c] = ldg16(base + (int64_t)Core::chunk_elem(c, ln) * EB);
 #pragma unroll
             for (int c = 0; c < CPL; ++c)
-                R.v[u][c] = ldg16((ok ? a + vdelta : dummy) + (int64_t)chunk_elem(c) * EB);
+                R.v[u][c] = ldg16((ok ? a + vdelta : dummy) + (int64_t)Core::chunk_elem(c, ln) * EB);
         }
     };
-    auto consume = [&](const Rows &R) {
-        float sc[U][G];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float kf[DT == QSA_BF16 ? 1 : EPL];
-            if constexpr (DT != QSA_BF16) {
-#pragma unroll
-                for (int c = 0; c < CPL; ++c)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        if constexpr (DT == QSA_F32)
-                            kf[c * EPC + i] = __uint_as_float(R.k[u][c][i]);
-                        else
-                            e4m3x4_to_f32(R.k[u][c][i], &kf[c * EPC + 4 * i]);
-                    }
-            }
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float d = 0.f;
-                if constexpr (DT == QSA_BF16) {
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qraw[h][c][i]), as_bf16x2(R.k[u][c][i]),
-                                                                d, false);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e)
-                        d = fmaf(qf[h][e], kf[e], d);
-                }
-                d = team_sum<TL>(d) * p.scale_log2;
-                sc[u][h] = R.ok[u] ? d : kNegInf;
-            }
-        }
-        // lazy rescale of the running state
-        float mx[G];
-        bool need = false;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            mx[h] = m[h];
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                mx[h] = fmaxf(mx[h], sc[u][h]);
-            need |= mx[h] > m[h] + kRescaleSlack;
-        }
-        if (__any(need)) {
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float alpha = __builtin_amdgcn_exp2f(m[h] - mx[h]);
-                l[h] *= alpha;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e)
-                    acc[h][e] *= alpha;
-                m[h] = mx[h];
-            }
-        }
-        if constexpr (kPaired) {
-#pragma unroll
-            for (int u = 0; u < U; u += 2) {
-                // (key u, key u+1) pairs of each V element
-                uint32_t vlo[CPL][4], vhi[CPL][4];
-#pragma unroll
-                for (int c = 0; c < CPL; ++c)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        vlo[c][i] = __builtin_amdgcn_perm(R.v[u + 1][c][i], R.v[u][c][i], 0x05040100u);
-                        vhi[c][i] = __builtin_amdgcn_perm(R.v[u + 1][c][i], R.v[u][c][i], 0x07060302u);
-                    }
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const uint32_t wp = pack_bf16x2(__builtin_amdgcn_exp2f(sc[u][h] - m[h]),
-                                                    __builtin_amdgcn_exp2f(sc[u + 1][h] - m[h]));
-                    l[h] += bf16_lo(wp) + bf16_hi(wp);
-                    const bf16x2_t w2 = as_bf16x2(wp);
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            float &a0 = acc[h][c * EPC + 2 * i];
-                            float &a1 = acc[h][c * EPC + 2 * i + 1];
-                            a0 = __builtin_amdgcn_fdot2_f32_bf16(w2, as_bf16x2(vlo[c][i]), a0, false);
-                            a1 = __builtin_amdgcn_fdot2_f32_bf16(w2, as_bf16x2(vhi[c][i]), a1, false);
-                        }
-                }
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float vf[EPL];
-#pragma unroll
-                for (int c = 0; c < CPL; ++c)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        if constexpr (DT == QSA_F32) {
-                            vf[c * EPC + i] = __uint_as_float(R.v[u][c][i]);
-                        } else if constexpr (DT == QSA_BF16) {
-                            vf[c * EPC + 2 * i] = bf16_lo(R.v[u][c][i]);
-                            vf[c * EPC + 2 * i + 1] = bf16_hi(R.v[u][c][i]);
-                        } else {
-                            e4m3x4_to_f32(R.v[u][c][i], &vf[c * EPC + 4 * i]);
-                        }
-                    }
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const float w = __builtin_amdgcn_exp2f(sc[u][h] - m[h]);
-                    l[h] += w;
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e)
-                        acc[h][e] = fmaf(w, vf[e], acc[h][e]);
-                }
-            }
-        }
-    };
+    auto consume = [&](const Rows &R) { st.consume(R, q, p.scale_log2); };
 
     // ---- the pipeline: iteration i issues entries(i+2), pages(i+1), rows(i) and
     // folds rows(i-1). Register sets alternate between even and odd iterations.
@@ -297,6 +140,8 @@ __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParam
         Rows R0, R1;
         load_entries(0, E0);
         load_entries(1, E1);
+        b = find_seq_pos_wave(p.row_off, LIST == KEYS_TOKEN_INDICES ? nullptr : p.cache_lengths, p.batch,
+                              (uint32_t)r, pos);
         load_pages(0, E0, P0);
         // iterations 0 and 1 are peeled so that the loop is entered with the same
         // loads in flight as at its back edge
@@ -321,34 +166,9 @@ __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParam
         }
     }
 
-    // merge the key slots of this wavefront (butterfly over teams of the same kv head:
-    // afterwards every such team holds the wavefront's state for its head)
-    auto merge_teams = [&](auto off_tag) {
-        constexpr int OFF = decltype(off_tag)::value;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float ma, mb, la, lb;
-            xor_pair<OFF>(m[h], ma, mb);
-            xor_pair<OFF>(l[h], la, lb);
-            const float mn = fmaxf(ma, mb);
-            const float ca = __builtin_amdgcn_exp2f(ma - mn);
-            const float cb = __builtin_amdgcn_exp2f(mb - mn);
-            l[h] = ca * la + cb * lb;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                float aa, ab;
-                xor_pair<OFF>(acc[h][e], aa, ab);
-                acc[h][e] = ca * aa + cb * ab;
-            }
-            m[h] = mn;
-        }
-    };
-    // teams of the same kv head sit TL*HB lanes apart
-    if constexpr (TL <= 4) if (4 >= TL * HB) merge_teams(std::integral_constant<int, 4>());
-    if constexpr (TL <= 8) if (8 >= TL * HB) merge_teams(std::integral_constant<int, 8>());
-    if constexpr (TL <= 16) if (16 >= TL * HB) merge_teams(std::integral_constant<int, 16>());
-    if constexpr (TL <= 32) if (32 >= TL * HB) merge_teams(std::integral_constant<int, 32>());
-    static_assert(TL >= 4, "team merge starts at 4-lane teams");
+    // merge the key slots of this wavefront (teams of the same kv head sit TL*HB
+    // lanes apart)
+    st.merge_teams(TL * HB);
 
     // merge the wavefronts through LDS: the key-slot-0 team of each kv head writes it
     const int HG = HB * G;                       // q heads of the workgroup
@@ -359,19 +179,20 @@ __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParam
         for (int h = 0; h < G; ++h) {
             const int hq = hh * G + h;
             if (ln == 0) {
-                s_ml[(wave * HG + hq) * 2] = m[h];
-                s_ml[(wave * HG + hq) * 2 + 1] = l[h];
+                s_ml[(wave * HG + hq) * 2] = st.m[h];
+                s_ml[(wave * HG + hq) * 2 + 1] = st.l[h];
             }
 #pragma unroll
             for (int c = 0; c < CPL; ++c)
 #pragma unroll
                 for (int e = 0; e < EPC; e += 4)
-                    *reinterpret_cast<float4 *>(&s_acc[(wave * HG + hq) * D + chunk_elem(c) + e]) =
-                        make_float4(acc[h][c * EPC + e], acc[h][c * EPC + e + 1], acc[h][c * EPC + e + 2],
-                                    acc[h][c * EPC + e + 3]);
+                    *reinterpret_cast<float4 *>(&s_acc[(wave * HG + hq) * D + Core::chunk_elem(c, ln) + e]) =
+                        make_float4(st.acc[h][c * EPC + e], st.acc[h][c * EPC + e + 1], st.acc[h][c * EPC + e + 2],
+                                    st.acc[h][c * EPC + e + 3]);
         }
     }
-    __syncthreads();
+    // (the loads of the batches past the end that the pipeline issued stay in flight)
+    lds_barrier();
     // each thread finishes two adjacent outputs
     for (int idx = tid; idx < HG * D / 2; idx += nthreads) {
         const int hq = (2 * idx) / D;
