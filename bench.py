@@ -354,6 +354,7 @@ def main():
         res["other_workloads"] = [
             other_workload("c3_prefill_bf16", W.c3_prefill_bf16, 1, dev, stream, n, 3),
             other_workload("c4_block_sparse_fp8", W.c4_block_sparse_fp8, 8, dev, stream, n, 3),
+            other_workload("c4s_block_sparse_spec_fp8", W.c4s_block_sparse_spec_fp8, 8, dev, stream, n, 3),
             other_workload("c5_latent_bf16", W.c5_latent_bf16, 4, dev, stream, n, 3),
         ]
     if not args.no_cpu_baseline:

@@ -124,7 +124,7 @@ gather_mfma_kernel(GatherParams p)
     uint16_t *s_v = reinterpret_cast<uint16_t *>(s_k + kTileKeys * KROWB);   // [32][VROW] bf16
 
     // prologue: list length, sequence and the q fragments go out together
-    const int64_t n = key_list_length_v<LIST>(p, r);
+    const int64_t n = key_list_length(p, r);
     const char *qrow0 = static_cast<const char *>(p.q) + ((r * p.num_q_heads + (int64_t)g * G) * D) * EB;
     const bool head_real = li < G;
     const char *qrow = head_real ? qrow0 + (int64_t)li * D * EB : qrow0;
@@ -139,8 +139,9 @@ gather_mfma_kernel(GatherParams p)
             qf[c] = head_real ? v : u32x2{0, 0};
         }
     }
-    int b = 0;              // sequence and position: found after the first list entries left
     int64_t pos = 0;
+    const int b = find_seq_pos_wave(p.row_off, LIST == KEYS_TOKEN_INDICES ? nullptr : p.cache_lengths, p.batch,
+                                    (uint32_t)r, pos);
     const int64_t j0 = (int64_t)s * p.split_keys;
     const int64_t jend = j0 + p.split_keys;
     const int64_t j1 = n < jend ? n : jend;
@@ -283,8 +284,6 @@ gather_mfma_kernel(GatherParams p)
         Rows R0, R1;
         load_entries(0, E0);
         load_entries(1, E1);
-        b = find_seq_pos_wave(p.row_off, LIST == KEYS_TOKEN_INDICES ? nullptr : p.cache_lengths, p.batch,
-                              (uint32_t)r, pos);
         load_pages(0, E0, P0);
         load_entries(2, E0);
         load_pages(1, E1, P1);

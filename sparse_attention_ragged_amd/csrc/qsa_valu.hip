@@ -70,7 +70,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParam
     const int NK = NW * KPW;                     // key slots per workgroup
 
     // prologue: list length and the q rows go out together
-    const int64_t n = key_list_length_v<LIST>(p, r);
+    const int64_t n = key_list_length(p, r);
     const char *qbase = static_cast<const char *>(p.q) + ((r * p.num_q_heads + (int64_t)g * G) * D) * EB;
     typename Core::Q q;
 #pragma unroll
@@ -78,8 +78,9 @@ __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParam
 #pragma unroll
         for (int c = 0; c < CPL; ++c)
             q.raw[h][c] = ldg16(qbase + ((int64_t)h * D + Core::chunk_elem(c, ln)) * EB);
-    int b = 0;              // sequence and position: found after the first list entries left
     int64_t pos = 0;
+    const int b = find_seq_pos_wave(p.row_off, LIST == KEYS_TOKEN_INDICES ? nullptr : p.cache_lengths, p.batch,
+                                    (uint32_t)r, pos);
     const int64_t j0 = (int64_t)s * p.split_keys;
     const int64_t jend = j0 + p.split_keys;
     const int64_t j1 = n < jend ? n : jend;
@@ -140,8 +141,6 @@ __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParam
         Rows R0, R1;
         load_entries(0, E0);
         load_entries(1, E1);
-        b = find_seq_pos_wave(p.row_off, LIST == KEYS_TOKEN_INDICES ? nullptr : p.cache_lengths, p.batch,
-                              (uint32_t)r, pos);
         load_pages(0, E0, P0);
         // iterations 0 and 1 are peeled so that the loop is entered with the same
         // loads in flight as at its back edge

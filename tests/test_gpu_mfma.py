@@ -127,6 +127,27 @@ def test_block_sparse_prefill_rows_and_splits():
         compare(got, ref, "e4m3", "block-sparse splits=%d" % splits)
 
 
+def test_block_sparse_speculative_decode_full_size():
+    """Speculative decode at the C4 shapes: 32 sequences x 3 draft tokens, each token at
+    its own position with its own top-16 blocks and causal clip (the pages route 2-4
+    query tokens per sequence to a separate kernel; here the one gather kernel takes
+    every row's position from its sequence's cache length and its index). All rows."""
+    announce("block-sparse spec decode: generating")
+    case = W.c4s_block_sparse_spec_fp8()
+    announce("block-sparse spec decode: running (%d rows)" % case.total_q)
+    got, ref, _ = run(case)
+    compare(got, ref, "e4m3", "block-sparse spec decode", rel_rms_max=0.02)
+
+
+def test_block_sparse_prefill_sampled_rows():
+    """Block-sparse prefill: 4 sequences x 96 new tokens, bf16, sampled rows."""
+    case = W.c4p_block_sparse_prefill_bf16()
+    rows = sorted(set(np.linspace(0, case.total_q - 1, 40).astype(int).tolist()) | {95, 96, 191, 192})
+    announce("block-sparse prefill: running (%d rows checked)" % len(rows))
+    got, ref, _ = run(case, rows=rows)
+    compare(got, ref, "bf16", "block-sparse prefill", rel_rms_max=0.01)
+
+
 def test_block_sparse_clip_never_reads_past_position():
     """Slots after a row's position in its last block hold NaN in the cache; the
     causal clip must keep them out of the result."""

@@ -426,6 +426,27 @@ def c4_block_sparse_fp8(seed=4, batch=32, cache_range=(16384, 32768)):
                              block_size=64, scale=1 / math.sqrt(128), std=0.5)
 
 
+def c4s_block_sparse_spec_fp8(seed=6, batch=32, draft=3, cache_range=(16384, 32768)):
+    """Block-sparse speculative decode: the C4 shapes with `draft` query tokens per
+    sequence, each at its own position (cache length + its index) with its own top-16
+    blocks and its own causal clip."""
+    rng = np.random.default_rng(seed + 10_000)
+    cl = rng.integers(cache_range[0], cache_range[1], size=batch, endpoint=True)
+    return make_block_sparse(name="c4s_block_sparse_spec_fp8", seed=seed, cache_lengths=cl, rows=[draft] * batch,
+                             page_size=128, num_kv_heads=4, group=8, head_dim=128, dtype="e4m3", topk=16,
+                             block_size=64, scale=1 / math.sqrt(128), std=0.5)
+
+
+def c4p_block_sparse_prefill_bf16(seed=7, batch=4, rows=96, cache_range=(4096, 16384)):
+    """Block-sparse prefill: `rows` new tokens per sequence (more than four: the pages'
+    prefill case), bf16, 32 q heads / 4 kv heads, top-16 of 64-token blocks."""
+    rng = np.random.default_rng(seed + 10_000)
+    cl = rng.integers(cache_range[0], cache_range[1], size=batch, endpoint=True)
+    return make_block_sparse(name="c4p_block_sparse_prefill_bf16", seed=seed, cache_lengths=cl, rows=[rows] * batch,
+                             page_size=128, num_kv_heads=4, group=8, head_dim=128, dtype="bf16", topk=16,
+                             block_size=64, scale=1 / math.sqrt(128), std=0.5)
+
+
 def c5_latent_bf16(seed=5, n_decode=16, n_prefill=4, prefill_rows=128, pos_range=(2048, 65536)):
     """Latent window + compressed + sink: one latent head, D 512, 64 q heads, bf16;
     16 decode rows + 4 x 128 prefill rows, positions U[2k,64k], window 128 (page 64),
@@ -444,6 +465,8 @@ NAMED = {
     "c2_decode_bf16": c2_decode_bf16,
     "c3_prefill_bf16": c3_prefill_bf16,
     "c4_block_sparse_fp8": c4_block_sparse_fp8,
+    "c4s_block_sparse_spec_fp8": c4s_block_sparse_spec_fp8,
+    "c4p_block_sparse_prefill_bf16": c4p_block_sparse_prefill_bf16,
     "c5_latent_bf16": c5_latent_bf16,
 }
 
