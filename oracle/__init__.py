@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for index-selected sparse attention over a paged KV cache.
+"""fp64 CPU oracle for index-selected sparse attention over a paged KV cache (and for
+dense ragged attention without a cache, the comparison row).
 
 TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package. The product library
@@ -67,7 +68,8 @@ def load(path: str = None):
                                    P, I64, I64, I64, I64, P, P, I64,
                                    P, I64, I64, I64, I64, P, I64,
                                    I64, I64, P, I64, P, F, I]
-        for f in (lib.orc_decode, lib.orc_qsa, lib.orc_block_sparse, lib.orc_latent):
+        lib.orc_dense.argtypes = [P, P, I64, P, P, P, I, I64, I64, I64, I64, P, I64, I, I64, F, I]
+        for f in (lib.orc_decode, lib.orc_qsa, lib.orc_block_sparse, lib.orc_latent, lib.orc_dense):
             f.restype = I
         _libs[path] = lib
     return _libs[path]
@@ -197,6 +199,24 @@ def latent_sparse_attention(*, q, dtype, input_row_offsets, swa, comp, layer_idx
     return out
 
 
+def dense_attention(*, q, k, v, dtype, input_row_offsets, causal, window, scale, rows=None,
+                    nthreads=None, lib=None) -> np.ndarray:
+    """Dense ragged attention without a KV cache ("RaggedFlashAttentionGPU"); fp64
+    [n_rows, Hq, D]. k, v: [total_q, Hkv, D] of ``dtype``; window <= 0 means none."""
+    lib = lib or load()
+    keep = _Keep()
+    total_q, Hq, D = q.shape
+    Hkv = k.shape[1]
+    rp, n = _rows_arg(keep, rows, total_q)
+    out = np.empty((n, Hq, D), np.float64)
+    off = np.asarray(input_row_offsets, np.uint32)
+    rc = lib.orc_dense(out.ctypes.data, rp, n, keep.ptr(q), keep.ptr(k), keep.ptr(v), DT[dtype], total_q, Hq,
+                       Hkv, D, keep.ptr(off), len(off) - 1, int(bool(causal)), int(window), scale,
+                       nthreads or default_threads())
+    _check(rc, "orc_dense")
+    return out
+
+
 def _leaf(c):
     return dict(blocks=c.storage, num_pages=c.num_pages, num_layers=c.num_layers,
                 page_size=c.page_size, num_kv_heads=c.num_kv_heads, page_stride=c.page_stride,
@@ -231,4 +251,8 @@ def run_case(case, rows=None, nthreads=None, lib=None) -> np.ndarray:
                                        window=case.window, comp_indices=case.comp_indices,
                                        attn_sink=case.attn_sink, scale=case.scale, rows=rows,
                                        nthreads=nthreads, lib=lib)
+    if case.kind == "dense":
+        return dense_attention(q=case.q, k=case.k, v=case.v, dtype=case.dtype,
+                               input_row_offsets=case.input_row_offsets, causal=case.causal,
+                               window=case.window, scale=case.scale, rows=rows, nthreads=nthreads, lib=lib)
     raise ValueError(case.kind)

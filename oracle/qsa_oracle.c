@@ -25,13 +25,21 @@
  *     (window keys max(0, pos-window+1)..pos, listed compressed entries with -1
  *     marking an unused slot, per-head sink logits, scale applied to scores).
  *
+   - "RaggedFlashAttentionGPU": summary, Parameters and Args (ragged q, k, v
+ *     [total_seq_len, heads, head_dim] without a KV cache, input_row_offsets,
+ *     a mask type and an optional local window size, -1 for none).
+ *
  * Readings where the pages are silent (listed in the design notes of the repo):
  *   - query head h reads kv head h / group (consecutive groups);
  *   - a row's position is cache_lengths[b] + (row - input_row_offsets[b]);
  *   - counts <= 0 gives an all-zero output row; counts > selection_width is
  *     clamped to selection_width; duplicated indices count with multiplicity;
  *   - latent leaves hold one plane: the same latent row is key and value;
- *   - the sink logit is not multiplied by scale and carries a zero value row.
+ *   - the sink logit is not multiplied by scale and carries a zero value row;
+ *   - dense ragged attention: row i of a sequence (0-based within it) sees the
+ *     keys j of its own sequence with j <= i under the causal mask (all j of the
+ *     sequence without a mask) and, with a local window w > 0, j >= i - w + 1;
+ *     k and v may have fewer heads than q (query head h reads kv head h / group).
  *
  * Parity pins: every function here is pinned by tests/test_oracle_pins.py
  * (closed forms, invariants, brute-force dense masked attention, exhaustive
@@ -404,6 +412,72 @@ int orc_latent(double *out, const int64_t *rows, int64_t n_rows,
             }
         }
         free(X);
+        free(s);
+        free(qv);
+    }
+    return err;
+}
+
+/* ------------------------------------------------------------ dense ragged */
+
+/* Dense ragged attention without a KV cache ("RaggedFlashAttentionGPU").
+ * For query row r of sequence b, i = r - row_off[b], L = row_off[b+1] - row_off[b]:
+ *   keys j in [lo, hi], hi = causal ? i : L - 1, lo = window > 0 ? max(0, i - window + 1) : 0,
+ *   K_j = k[row_off[b] + j, h / group, :], V_j likewise; softmax(scale * q.K) . V. */
+int orc_dense(double *out, const int64_t *rows, int64_t n_rows,
+              const void *q, const void *k, const void *v, int dt, int64_t total_q, int64_t Hq,
+              int64_t Hkv, int64_t D, const uint32_t *row_off, int64_t batch, int causal,
+              int64_t window, float scale, int nthreads)
+{
+    if (Hkv <= 0 || Hq % Hkv || check_rows(rows, n_rows, total_q))
+        return ORC_EINPUT;
+    int64_t G = Hq / Hkv;
+    int64_t maxlen = 1;
+    for (int64_t b = 0; b < batch; ++b)
+        if ((int64_t)row_off[b + 1] - (int64_t)row_off[b] > maxlen)
+            maxlen = (int64_t)row_off[b + 1] - (int64_t)row_off[b];
+    int err = ORC_OK;
+#pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1)
+    {
+        double *K = malloc(sizeof(double) * maxlen * D);
+        double *V = malloc(sizeof(double) * maxlen * D);
+        double *s = malloc(sizeof(double) * maxlen);
+        double *qv = malloc(sizeof(double) * D);
+        if (!K || !V || !s || !qv) {
+#pragma omp atomic write
+            err = ORC_ENOMEM;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < n_rows; ++i) {
+            if (err)
+                continue;
+            int64_t r = rows ? rows[i] : i;
+            int64_t b = seq_of_row(row_off, batch, r);
+            if (b < 0) {
+#pragma omp atomic write
+                err = ORC_EINPUT;
+                continue;
+            }
+            int64_t start = row_off[b], len = (int64_t)row_off[b + 1] - start, t = r - start;
+            int64_t hi = causal ? t : len - 1;
+            int64_t lo = window > 0 && t - window + 1 > 0 ? t - window + 1 : 0;
+            int64_t n = hi - lo + 1;
+            double *o = out + i * Hq * D;
+            for (int64_t g = 0; g < Hkv; ++g) {
+                for (int64_t j = 0; j < n; ++j)
+                    for (int64_t d = 0; d < D; ++d) {
+                        K[j * D + d] = elem(k, dt, ((start + lo + j) * Hkv + g) * D + d);
+                        V[j * D + d] = elem(v, dt, ((start + lo + j) * Hkv + g) * D + d);
+                    }
+                for (int64_t h = g * G; h < (g + 1) * G; ++h) {
+                    for (int64_t d = 0; d < D; ++d)
+                        qv[d] = elem(q, dt, (r * Hq + h) * D + d);
+                    attend(qv, K, V, n, D, (double)scale, -INFINITY, s, o + h * D);
+                }
+            }
+        }
+        free(K);
+        free(V);
         free(s);
         free(qv);
     }

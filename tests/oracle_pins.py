@@ -13,7 +13,9 @@ Kinds of pin (none re-types the oracle's formula):
   * special cases that reduce to a library routine (torch's scaled_dot_product_attention
     with a causal or sliding-window mask, in float64 on the CPU);
   * invariants (page permutation, garbage past counts, index order, GQA expansion,
-    sink as a closed-form factor, block-sparse as a token selection).
+    sink as a closed-form factor, block-sparse as a token selection);
+  * dense ragged attention (no cache) against torch SDPA with causal, sliding-window
+    and empty masks per sequence, and the one-key closed forms.
 """
 from __future__ import annotations
 
@@ -556,6 +558,74 @@ def pin_latent_unused_slots_anywhere(lib):
         ci[r, :len(v)] = v
     got = oracle.run_case(clone_case(case, comp_indices=ci), lib=lib)
     assert np.array_equal(got, base)
+
+
+# ------------------------------------------------------------------ pins: dense ragged
+
+def _dense_sdpa(case, mask_of):
+    """Per sequence: torch SDPA in float64 with GQA expanded by repetition and the mask
+    mask_of(i, j) over the sequence's own rows (i) and keys (j)."""
+    off = case.input_row_offsets
+    G = case.num_q_heads // case.k.shape[1]
+    q = q64(case)
+    k = case.k.to(torch.float32).to(torch.float64).numpy()
+    v = case.v.to(torch.float32).to(torch.float64).numpy()
+    out = np.zeros_like(q)
+    for b in range(case.batch):
+        a0, a1 = int(off[b]), int(off[b + 1])
+        L = a1 - a0
+        if L == 0:
+            continue
+        i = np.arange(L)[:, None]
+        j = np.arange(L)[None, :]
+        kk = np.repeat(k[a0:a1].transpose(1, 0, 2), G, axis=0)
+        vv = np.repeat(v[a0:a1].transpose(1, 0, 2), G, axis=0)
+        ref = sdpa64(q[a0:a1].transpose(1, 0, 2), kk, vv, mask_of(i, j), case.scale)
+        out[a0:a1] = ref.transpose(1, 0, 2)
+    return out
+
+
+def _dense_case(seed, rows, causal, window, hkv=2, group=2, d=16, dtype="bf16"):
+    return W.make_dense(name="dense_pin", seed=seed, rows=rows, num_kv_heads=hkv, group=group, head_dim=d,
+                        dtype=dtype, out_dtype="f32", causal=causal, window=window, scale=0.3)
+
+
+def pin_dense_causal_is_sdpa(lib):
+    """Causal dense ragged attention equals torch SDPA with a lower-triangular mask per
+    sequence (keys of other sequences never enter)."""
+    case = _dense_case(41, [7, 1, 12, 4], True, -1)
+    got = oracle.run_case(case, lib=lib)
+    assert_close(got, _dense_sdpa(case, lambda i, j: j <= i), 1e-12, "dense causal vs SDPA")
+
+
+def pin_dense_no_mask_is_sdpa(lib):
+    case = _dense_case(42, [5, 9, 3], False, -1, hkv=1, group=4, dtype="f32")
+    got = oracle.run_case(case, lib=lib)
+    assert_close(got, _dense_sdpa(case, lambda i, j: np.ones_like(i + j, bool)), 1e-12, "dense no mask vs SDPA")
+
+
+def pin_dense_sliding_window_is_sdpa(lib):
+    """A local window w keeps keys i - w + 1 <= j (with j <= i under the causal mask)."""
+    for w in (1, 3, 6):
+        case = _dense_case(43 + w, [11, 2, 8], True, w, hkv=2, group=1)
+        got = oracle.run_case(case, lib=lib)
+        ref = _dense_sdpa(case, lambda i, j, w=w: (j <= i) & (j >= i - w + 1))
+        assert_close(got, ref, 1e-12, "dense window %d vs SDPA" % w)
+    case = _dense_case(49, [9, 5], False, 3, hkv=1, group=2)
+    got = oracle.run_case(case, lib=lib)
+    assert_close(got, _dense_sdpa(case, lambda i, j: j >= i - 2), 1e-12, "dense window, no causal mask")
+
+
+def pin_dense_first_row_and_unit_window_are_v_rows(lib):
+    """Closed forms: the first row of a causal sequence and every row under a window of
+    one see exactly one key, so their output is that key's V row (every q head)."""
+    case = _dense_case(50, [6, 3], True, 1, hkv=2, group=3, d=8, dtype="f32")
+    got = oracle.run_case(case, lib=lib)
+    v = case.v.double().numpy()
+    G = 3
+    for r in range(case.total_q):
+        for h in range(case.num_q_heads):
+            assert_close(got[r, h], v[r, h // G], 0.0, "window 1 row %d head %d" % (r, h))
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

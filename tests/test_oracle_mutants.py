@@ -39,6 +39,13 @@ MUTANTS = [
     ("e4m3_subnormal", "ldexp((double)m, -9)", "ldexp((double)m, -10)"),
     ("normalise_dropped", "out[d] /= z;", "out[d] /= 1.0;"),
     ("max_not_subtracted_consistently", "z += w;", "z += w * 1.0000001;"),
+    ("dense_causal_off_by_one", "int64_t hi = causal ? t : len - 1;", "int64_t hi = causal ? t - 1 : len - 1;"),
+    ("dense_mask_ignored", "int64_t hi = causal ? t : len - 1;", "int64_t hi = len - 1;"),
+    ("dense_window_off_by_one", "t - window + 1 > 0 ? t - window + 1 : 0", "t - window > 0 ? t - window : 0"),
+    ("dense_other_sequence", "K[j * D + d] = elem(k, dt, ((start + lo + j) * Hkv + g) * D + d);",
+     "K[j * D + d] = elem(k, dt, ((lo + j) * Hkv + g) * D + d);"),
+    ("dense_kv_head_dropped", "V[j * D + d] = elem(v, dt, ((start + lo + j) * Hkv + g) * D + d);",
+     "V[j * D + d] = elem(v, dt, ((start + lo + j) * Hkv + 0) * D + d);"),
 ]
 
 

@@ -119,7 +119,7 @@ class PagedCache:
 
 @dataclass
 class Case:
-    """One call's worth of inputs. ``kind`` is "qsa", "block_sparse" or "latent"."""
+    """One call's worth of inputs. ``kind`` is "qsa", "block_sparse", "latent" or "dense"."""
     kind: str
     name: str
     seed: int
@@ -128,7 +128,7 @@ class Case:
     q: torch.Tensor                  # [total_q, Hq, D]
     input_row_offsets: np.ndarray    # [batch+1] uint32
     max_prompt_length: int
-    kv: PagedCache                   # qsa/block_sparse: the K/V cache; latent: the window leaf
+    kv: Optional[PagedCache]         # qsa/block_sparse: the K/V cache; latent: the window leaf; dense: None
     layer_idx: int
     scale: float
     # qsa
@@ -142,6 +142,10 @@ class Case:
     window: int = 0
     comp_indices: Optional[np.ndarray] = None    # [total_q, num_comp] int32
     attn_sink: Optional[np.ndarray] = None       # [Hq] float32
+    # dense (no cache): k, v [total_q, Hkv, D]; causal mask; window (latent too) <= 0: none
+    k: Optional[torch.Tensor] = None
+    v: Optional[torch.Tensor] = None
+    causal: bool = True
     meta: dict = field(default_factory=dict)
 
     @property
@@ -328,6 +332,22 @@ def make_block_sparse(*, name="block_sparse", seed, cache_lengths, page_size, nu
                 meta={"group": group, "topk": topk})
 
 
+# --------------------------------------------------------------------------- dense
+
+def make_dense(*, name="dense", seed, rows, num_kv_heads, group, head_dim, dtype, out_dtype, causal=True,
+               window=-1, scale, std=1.0) -> Case:
+    """Dense ragged attention inputs without a KV cache ("RaggedFlashAttentionGPU"): q
+    [total, Hkv*group, D], k and v [total, Hkv, D], N(0, std^2); rows per sequence."""
+    rows = [int(x) for x in rows]
+    off = _row_offsets(rows)
+    total = int(off[-1])
+    q = _normal((total, num_kv_heads * group, head_dim), seed, 2, std, dtype)
+    k = _normal((total, num_kv_heads, head_dim), seed, 3, std, dtype)
+    v = _normal((total, num_kv_heads, head_dim), seed, 4, std, dtype)
+    return Case("dense", name, seed, dtype, out_dtype, q, off, max(rows), None, 0, float(np.float32(scale)),
+                window=int(window), k=k, v=v, causal=bool(causal), meta={"group": group})
+
+
 # --------------------------------------------------------------------------- latent
 
 def make_latent(*, name="latent", seed, decode_positions, prefill_positions, prefill_rows,
@@ -447,6 +467,17 @@ def c4p_block_sparse_prefill_bf16(seed=7, batch=4, rows=96, cache_range=(4096, 1
                              block_size=64, scale=1 / math.sqrt(128), std=0.5)
 
 
+def f3_dense_prefill_bf16(seed=8, batch=8, rows_range=(256, 2048)):
+    """Dense causal ragged attention at the C3 prefill shapes (no cache): rows
+    U[256, 2048] per sequence, 64 q heads / 4 kv heads, D 128, bf16; the sparse-vs-dense
+    comparison at equal shapes."""
+    rng = np.random.default_rng(3 + 10_000)          # C3's row draw
+    rows = rng.integers(rows_range[0], rows_range[1], size=batch, endpoint=True)
+    return make_dense(name="f3_dense_prefill_bf16", seed=seed, rows=rows, num_kv_heads=4, group=16,
+                      head_dim=128, dtype="bf16", out_dtype="bf16", causal=True, window=-1,
+                      scale=1 / math.sqrt(128))
+
+
 def c5_latent_bf16(seed=5, n_decode=16, n_prefill=4, prefill_rows=128, pos_range=(2048, 65536)):
     """Latent window + compressed + sink: one latent head, D 512, 64 q heads, bf16;
     16 decode rows + 4 x 128 prefill rows, positions U[2k,64k], window 128 (page 64),
@@ -468,6 +499,7 @@ NAMED = {
     "c4s_block_sparse_spec_fp8": c4s_block_sparse_spec_fp8,
     "c4p_block_sparse_prefill_bf16": c4p_block_sparse_prefill_bf16,
     "c5_latent_bf16": c5_latent_bf16,
+    "f3_dense_prefill_bf16": f3_dense_prefill_bf16,
 }
 
 
@@ -484,6 +516,8 @@ def gathered_kv_bytes(case: Case) -> int:
         W = case.token_indices.shape[1]
         n = np.clip(case.counts.astype(np.int64), 0, W).sum()
         return int(n) * case.kv.num_kv_heads * 2 * D * eb
+    if case.kind == "dense":
+        return int(dense_key_counts(case).sum()) * case.k.shape[1] * 2 * D * eb
     pos = case.positions()
     if case.kind == "block_sparse":
         bs = case.block_size
@@ -496,3 +530,17 @@ def gathered_kv_bytes(case: Case) -> int:
         comp = (case.comp_indices >= 0).sum()
         return int(win + comp) * D * eb
     raise ValueError(case.kind)
+
+
+def dense_key_counts(case: Case) -> np.ndarray:
+    """Keys each row of a dense case attends to (its own sequence only): [lo, hi] with
+    hi = i (causal) or L - 1, lo = max(0, i - window + 1) when window > 0."""
+    off = case.input_row_offsets.astype(np.int64)
+    n = np.empty(case.total_q, np.int64)
+    for b in range(case.batch):
+        L = off[b + 1] - off[b]
+        i = np.arange(L)
+        hi = i if case.causal else np.full(L, L - 1)
+        lo = np.maximum(0, i - case.window + 1) if case.window > 0 else np.zeros(L, np.int64)
+        n[off[b]:off[b + 1]] = hi - lo + 1
+    return n
