@@ -146,6 +146,12 @@ def algorithmic(case):
         per_unit = 2 * D * eb
         flops = units * 4 * D * (Hq // case.kv.num_kv_heads)
         unit = "(query row, kv head, key in a listed block): 2*D*elem K/V bytes"
+    elif case.kind == "dense":
+        hkv = case.k.shape[1]
+        units = int(W.dense_key_counts(case).sum())
+        per_unit = hkv * 2 * D * eb
+        flops = units * 4 * D * Hq
+        unit = "(query row, key of its sequence): Hkv*2*D*elem K/V bytes"
     else:
         units = gathered // (D * eb)
         per_unit = D * eb
@@ -356,6 +362,7 @@ def main():
             other_workload("c4_block_sparse_fp8", W.c4_block_sparse_fp8, 8, dev, stream, n, 3),
             other_workload("c4s_block_sparse_spec_fp8", W.c4s_block_sparse_spec_fp8, 8, dev, stream, n, 3),
             other_workload("c5_latent_bf16", W.c5_latent_bf16, 4, dev, stream, n, 3),
+            other_workload("f3_dense_prefill_bf16", W.f3_dense_prefill_bf16, 1, dev, stream, n, 3),
         ]
     if not args.no_cpu_baseline:
         log("cpu baseline (~%.0f s)" % args.cpu_seconds)

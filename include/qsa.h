@@ -1,7 +1,8 @@
 /*
  * qsa.h - C ABI of the MI355X (gfx950) sparse paged attention library.
  *
- * Three operations over a ragged batch of query rows and a paged KV cache:
+ * Three operations over a ragged batch of query rows and a paged KV cache, and the
+ * dense ragged attention they are compared with:
  *
  *   qsa_sparse_attention         index-selected sparse GQA: every query row attends
  *                                to the positions its token_indices row lists
@@ -204,6 +205,34 @@ qsa_status qsa_latent_sparse_attention(void *out, int32_t out_dtype, const qsa_r
                                        const float *attn_sink, float scale,
                                        const qsa_launch_options *opts, void *workspace,
                                        size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------- */
+/* Dense ragged attention without a KV cache ("RaggedFlashAttentionGPU": summary,
+ * Parameters and Args), the dense comparison for the sparse operations above.
+ *
+ * Row r, the i-th row of its sequence b (L = input_row_offsets[b+1] -
+ * input_row_offsets[b] rows), attends to the rows i' of the same sequence with
+ * i' <= i when causal (every i' < L when not) and i' >= i - window + 1 when
+ * window > 0; key i' is k[input_row_offsets[b] + i', h / group, :], value likewise.
+ *
+ *   out      [total_q, num_q_heads, head_dim] of out_dtype (QSA_F32 or QSA_BF16)
+ *   q        q->dtype in {F32, BF16, FP8_E4M3}; q->max_prompt_length (host) must be at
+ *            least the longest sequence (the pages' q_max_seq_len; it sizes the
+ *            split plan, and keys past it would not be visited)
+ *   k, v     [total_q, num_kv_heads, head_dim] of q->dtype, 16-byte aligned
+ *   causal   0 (no mask) or 1 (causal)
+ *   window   -1 for none, else >= 1 (the pages' local_window_size)
+ * Supported: the same (dtype, group, head_dim) as qsa_sparse_attention; groups of
+ * more than 16 are not built here. The dynamic schedule is refused.
+ */
+qsa_status qsa_ragged_attention_workspace_size(const qsa_ragged_q *q, int64_t num_kv_heads, int32_t causal,
+                                               int64_t window, const qsa_launch_options *opts,
+                                               size_t *bytes);
+
+qsa_status qsa_ragged_attention(void *out, int32_t out_dtype, const qsa_ragged_q *q, const void *k,
+                                const void *v, int64_t num_kv_heads, int32_t causal, int64_t window,
+                                float scale, const qsa_launch_options *opts, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------- */
 /* Text describing the last non-OK status returned on the calling thread. */

@@ -37,6 +37,7 @@ EXPORTS = (
     "qsa_sparse_attention_workspace_size", "qsa_sparse_attention",
     "qsa_block_sparse_attention_workspace_size", "qsa_block_sparse_attention",
     "qsa_latent_sparse_attention_workspace_size", "qsa_latent_sparse_attention",
+    "qsa_ragged_attention_workspace_size", "qsa_ragged_attention",
     "qsa_last_error", "qsa_abi_version", "qsa_struct_size", "qsa_set_timing_events",
 )
 
@@ -90,9 +91,12 @@ def _load():
     lib.qsa_latent_sparse_attention_workspace_size.argtypes = [pr, I64, I64, po, ctypes.POINTER(SZ)]
     lib.qsa_latent_sparse_attention.argtypes = [P, I32, pr, pc, pc, ctypes.c_uint32, I64, P, I64, P, F,
                                                 po, P, SZ, P]
+    lib.qsa_ragged_attention_workspace_size.argtypes = [pr, I64, I32, I64, po, ctypes.POINTER(SZ)]
+    lib.qsa_ragged_attention.argtypes = [P, I32, pr, P, P, I64, I32, I64, F, po, P, SZ, P]
     for name in ("qsa_sparse_attention_workspace_size", "qsa_sparse_attention",
                  "qsa_block_sparse_attention_workspace_size", "qsa_block_sparse_attention",
-                 "qsa_latent_sparse_attention_workspace_size", "qsa_latent_sparse_attention"):
+                 "qsa_latent_sparse_attention_workspace_size", "qsa_latent_sparse_attention",
+                 "qsa_ragged_attention_workspace_size", "qsa_ragged_attention"):
         getattr(lib, name).restype = ctypes.c_int
     lib.qsa_last_error.restype = ctypes.c_char_p
     lib.qsa_abi_version.restype = I32
@@ -306,6 +310,41 @@ def latent_sparse_attention(q, input_row_offsets, swa: PagedCache, comp: PagedCa
         out.data_ptr(), DTYPE_CODE[out_dtype], ctypes.byref(rq), ctypes.byref(cs), ctypes.byref(cc),
         layer_idx, window, comp_indices.data_ptr(), num_comp, attn_sink.data_ptr(), scale, o,
         ws.data_ptr() if ws is not None else None, wsb, _stream(q, stream)))
+    return out
+
+
+def ragged_attention_workspace_size(q, input_row_offsets, num_kv_heads: int, causal: bool = True,
+                                    window: int = -1, max_prompt_length: int = 0, options=None) -> int:
+    n = ctypes.c_size_t(0)
+    rq = _ragged(q, input_row_offsets, max_prompt_length)
+    _check(lib.qsa_ragged_attention_workspace_size(ctypes.byref(rq), num_kv_heads, int(bool(causal)), window,
+                                                   _opts(options), ctypes.byref(n)))
+    return n.value
+
+
+def ragged_attention(q, k, v, input_row_offsets, scale: float, *, causal: bool = True, window: int = -1,
+                     out_dtype=None, max_prompt_length: int, options=None, out=None, workspace=None,
+                     stream=None) -> torch.Tensor:
+    """Dense ragged attention without a KV cache; q [total, Hq, D], k/v [total, Hkv, D].
+    max_prompt_length (host) must be at least the longest sequence. Returns out."""
+    out_dtype = out_dtype or (q.dtype if q.dtype != torch.float8_e4m3fn else torch.bfloat16)
+    _need_gpu(k, v)
+    if k.dtype != q.dtype or v.dtype != q.dtype or k.shape != v.shape or k.dim() != 3:
+        raise ValueError("k and v must be [total, num_kv_heads, head_dim] of q's dtype")
+    if k.shape[0] != q.shape[0] or k.shape[2] != q.shape[2]:
+        raise ValueError("k and v must have q's rows and head_dim")
+    if not (k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("k and v must be contiguous")
+    rq = _ragged(q, input_row_offsets, max_prompt_length)
+    o = _opts(options)
+    n = ctypes.c_size_t(0)
+    _check(lib.qsa_ragged_attention_workspace_size(ctypes.byref(rq), k.shape[1], int(bool(causal)), window, o,
+                                                   ctypes.byref(n)))
+    ws, wsb = _workspace(n.value, q.device, workspace)
+    out = _out(q, out_dtype, out)
+    _check(lib.qsa_ragged_attention(
+        out.data_ptr(), DTYPE_CODE[out_dtype], ctypes.byref(rq), k.data_ptr(), v.data_ptr(), k.shape[1],
+        int(bool(causal)), window, scale, o, ws.data_ptr() if ws is not None else None, wsb, _stream(q, stream)))
     return out
 
 

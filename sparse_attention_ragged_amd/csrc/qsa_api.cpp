@@ -14,6 +14,8 @@ using namespace qsa;
 
 namespace {
 
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
 thread_local void *t_ev_start = nullptr;
 thread_local void *t_ev_stop = nullptr;
 
@@ -123,6 +125,34 @@ qsa_status block_plan(const qsa_ragged_q *q, const qsa_paged_cache *kv, int64_t 
     if (s == QSA_OK)
         s = plan_gather(q, kv->num_kv_heads, q->dtype, KEYS_BLOCKS, topk * block_size, block_size, opts, plan);
     return s;
+}
+
+qsa_status dense_plan(const qsa_ragged_q *q, int64_t num_kv_heads, int32_t causal, int64_t window,
+                      const qsa_launch_options *opts, Plan *plan)
+{
+    if (!q)
+        return fail(QSA_ERR_NULL, "q descriptor is NULL");
+    if (!q->input_row_offsets)
+        return fail(QSA_ERR_NULL, "input_row_offsets is required");
+    if (q->total_q < 0 || q->batch < 1 || q->num_q_heads < 1 || q->head_dim < 1)
+        return fail(QSA_ERR_SHAPE, "q: total_q >= 0, batch >= 1, num_q_heads >= 1, head_dim >= 1");
+    if (q->total_q > (int64_t(1) << 31) - 1 || q->batch > (int64_t(1) << 31) - 1 || q->num_q_heads > 65536)
+        return fail(QSA_ERR_SHAPE, "q: total_q, batch or num_q_heads out of range");
+    if (num_kv_heads < 1 || q->num_q_heads % num_kv_heads != 0)
+        return fail(QSA_ERR_SHAPE, "num_q_heads %lld is not a multiple of num_kv_heads %lld",
+                    (long long)q->num_q_heads, (long long)num_kv_heads);
+    if (causal != 0 && causal != 1)
+        return fail(QSA_ERR_SHAPE, "causal must be 0 or 1");
+    if (window != -1 && window < 1)
+        return fail(QSA_ERR_SHAPE, "window must be -1 (none) or >= 1");
+    if (q->dtype != QSA_F32 && q->dtype != QSA_BF16 && q->dtype != QSA_FP8_E4M3)
+        return fail(QSA_ERR_DTYPE, "q dtype %d is not accepted", q->dtype);
+    if (q->total_q > 0 && q->max_prompt_length < 1)
+        return fail(QSA_ERR_SHAPE, "max_prompt_length must be at least the longest sequence");
+    int64_t cap = q->max_prompt_length;
+    if (causal && window > 0 && window < cap)
+        cap = window;
+    return plan_gather(q, num_kv_heads, q->dtype, KEYS_DENSE, cap, 1, opts, plan);
 }
 
 qsa_status latent_plan(const qsa_ragged_q *q, int64_t window, int64_t num_comp,
@@ -312,6 +342,48 @@ size_t qsa_struct_size(int32_t which)
     case 2: return sizeof(qsa_launch_options);
     default: return 0;
     }
+}
+
+qsa_status qsa_ragged_attention_workspace_size(const qsa_ragged_q *q, int64_t num_kv_heads, int32_t causal,
+                                               int64_t window, const qsa_launch_options *opts, size_t *bytes)
+{
+    clear_error();
+    if (!bytes)
+        return fail(QSA_ERR_NULL, "bytes is NULL");
+    Plan plan;
+    qsa_status s = dense_plan(q, num_kv_heads, causal, window, opts, &plan);
+    *bytes = s == QSA_OK ? plan.ws_bytes : 0;
+    return s;
+}
+
+qsa_status qsa_ragged_attention(void *out, int32_t out_dtype, const qsa_ragged_q *q, const void *k,
+                                const void *v, int64_t num_kv_heads, int32_t causal, int64_t window,
+                                float scale, const qsa_launch_options *opts, void *workspace,
+                                size_t workspace_bytes, void *stream)
+{
+    clear_error();
+    Plan plan;
+    qsa_status s = dense_plan(q, num_kv_heads, causal, window, opts, &plan);
+    if (s != QSA_OK)
+        return s;
+    if ((s = check_out(out, out_dtype, q)) != QSA_OK)
+        return s;
+    if (q->total_q > 0 && (!q->q || !k || !v))
+        return fail(QSA_ERR_NULL, "q, k and v are required");
+    if (q->total_q > 0 && (!aligned16(q->q) || !aligned16(k) || !aligned16(v)))
+        return fail(QSA_ERR_SHAPE, "q, k and v must be 16-byte aligned");
+    if (!std::isfinite(scale))
+        return fail(QSA_ERR_SHAPE, "scale must be finite");
+    if ((s = check_workspace(plan, workspace, workspace_bytes)) != QSA_OK)
+        return s;
+    GatherParams p;
+    fill_common(p, out, out_dtype, q, num_kv_heads, 0, scale, plan, workspace);
+    p.list_kind = KEYS_DENSE;
+    p.dense_k = k;
+    p.dense_v = v;
+    p.dense_causal = causal;
+    p.window = window > 0 ? window : 0;
+    return run(p, plan, stream);
 }
 
 void qsa_set_timing_events(void *start, void *stop)

@@ -218,6 +218,19 @@ __device__ __forceinline__ int64_t key_list_length_v(const GatherParams &p, int6
     }
 }
 
+// Dense ragged attention ("RaggedFlashAttentionGPU"): row r, the i-th of its sequence
+// b (L rows starting at row_off[b]), sees the keys i' of the same sequence with
+// i' <= i under the causal mask (all of them without) and i' >= i - window + 1 for a
+// window > 0. Returns their number and sets `first` to the row index of the first one.
+__device__ __forceinline__ int64_t dense_key_range(const GatherParams &p, int64_t r, int b, int64_t &first)
+{
+    const int64_t start = p.row_off[b], len = (int64_t)p.row_off[b + 1] - start, i = r - start;
+    const int64_t hi = p.dense_causal ? i : len - 1;
+    const int64_t lo = p.window > 0 && i - p.window + 1 > 0 ? i - p.window + 1 : 0;
+    first = start + lo;
+    return hi >= lo ? hi - lo + 1 : 0;
+}
+
 // Number of keys in the list of row r (before splitting).
 __device__ __forceinline__ int64_t key_list_length(const GatherParams &p, int64_t r)
 {
@@ -280,6 +293,8 @@ __device__ __forceinline__ KeyPos key_pos(const GatherParams &p, int64_t pos, in
         const bool win = jj < p.window;
         k.tok = win ? (int32_t)(pos - p.window + 1 + jj) : raw;
         k.comp = !win;
+    } else if constexpr (LIST == KEYS_DENSE) {
+        k.tok = (int32_t)(pos + jj);   // row index of the key in the ragged k/v (pos = the row's first key)
     }
     k.present = k.present && k.tok >= 0;
     return k;
@@ -342,6 +357,12 @@ template <int EB, int LIST>
 __device__ __forceinline__ const char *row_address(const GatherParams &p, const KeyPos &k, uint32_t page,
                                                    int32_t slot, int g, const char *dummy, bool &present)
 {
+    if constexpr (LIST == KEYS_DENSE) {
+        present = k.present;
+        return present ? static_cast<const char *>(p.dense_k) +
+                             ((int64_t)k.tok * p.num_kv_heads + g) * (int64_t)p.head_dim * EB
+                       : dummy;
+    }
     const uint32_t head_b = LIST == KEYS_LATENT ? 0u : (uint32_t)(g * p.head_dim * EB);
     bool in;
     const char *a = leaf_row(p.kv, page, slot, head_b, in);

@@ -46,6 +46,7 @@ enum KeyList : int32_t {
     KEYS_TOKEN_INDICES = 0,  // token_indices[r, 0:min(counts[r], W)]
     KEYS_BLOCKS = 1,         // block ids d_indices[g, r, 0:topk], block_size keys each, clipped at pos
     KEYS_LATENT = 2,         // window positions then comp_indices[r, :] >= 0
+    KEYS_DENSE = 3,          // keys lo..hi of the row's own sequence in ragged k/v (no cache, no list)
 };
 
 struct GatherParams {
@@ -71,6 +72,9 @@ struct GatherParams {
     int64_t width;                   // W, topk or num_comp
     int64_t window;                  // latent window
     const float *sink;               // latent sink logits or NULL
+    const void *dense_k;             // dense: k, v [total_q, num_kv_heads, head_dim]
+    const void *dense_v;
+    int32_t dense_causal;            // dense: causal mask (the window is `window`, <= 0: none)
     float scale_log2;                // scale * log2(e)
     int32_t num_splits;
     int32_t waves;

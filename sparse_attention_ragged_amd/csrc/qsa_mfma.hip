@@ -124,7 +124,7 @@ gather_mfma_kernel(GatherParams p)
     uint16_t *s_v = reinterpret_cast<uint16_t *>(s_k + kTileKeys * KROWB);   // [32][VROW] bf16
 
     // prologue: list length, sequence and the q fragments go out together
-    const int64_t n = key_list_length(p, r);
+    int64_t n = LIST == KEYS_DENSE ? 0 : key_list_length(p, r);
     const char *qrow0 = static_cast<const char *>(p.q) + ((r * p.num_q_heads + (int64_t)g * G) * D) * EB;
     const bool head_real = li < G;
     const char *qrow = head_real ? qrow0 + (int64_t)li * D * EB : qrow0;
@@ -140,13 +140,18 @@ gather_mfma_kernel(GatherParams p)
         }
     }
     int64_t pos = 0;
-    const int b = find_seq_pos_wave(p.row_off, LIST == KEYS_TOKEN_INDICES ? nullptr : p.cache_lengths, p.batch,
-                                    (uint32_t)r, pos);
+    const int b = find_seq_pos_wave(p.row_off,
+                                    LIST == KEYS_TOKEN_INDICES || LIST == KEYS_DENSE ? nullptr : p.cache_lengths,
+                                    p.batch, (uint32_t)r, pos);
+    if constexpr (LIST == KEYS_DENSE)
+        n = dense_key_range(p, r, b, pos);     // pos: row index of the row's first key
     const int64_t j0 = (int64_t)s * p.split_keys;
     const int64_t jend = j0 + p.split_keys;
     const int64_t j1 = n < jend ? n : jend;
     const int nb = j1 > j0 ? (int)((j1 - j0 + kTileKeys - 1) / kTileKeys) : 0;
-    const int64_t vdelta = LIST == KEYS_LATENT ? 0 : (int64_t)p.kv.plane_stride_b;
+    const int64_t vdelta = LIST == KEYS_LATENT  ? 0
+                           : LIST == KEYS_DENSE ? static_cast<const char *>(p.dense_v) - static_cast<const char *>(p.dense_k)
+                                                : (int64_t)p.kv.plane_stride_b;
     const char *dummy = qrow0;                   // a readable row for absent keys
 
     float m = kNoKey, lsum = 0.f;                // head li (shared by the 4 lanes of li)
@@ -169,12 +174,20 @@ gather_mfma_kernel(GatherParams p)
     auto key_index = [&](int batch) -> int64_t { return j0 + (int64_t)batch * kTileKeys + kl; };
     auto load_entries = [&](int batch, Entries &E) {
         const int64_t jj = key_index(batch);
-        E.raw = *entry_ptr<LIST>(p, r, g, jj, jj < j1);
+        if constexpr (LIST == KEYS_DENSE)
+            E.raw = 0;                             // dense: the key is its index, nothing to load
+        else
+            E.raw = *entry_ptr<LIST>(p, r, g, jj, jj < j1);
     };
     auto load_pages = [&](int batch, const Entries &E, Pages &P) {
         const int64_t jj = key_index(batch);
         P.k = key_pos<LIST>(p, pos, jj, E.raw, jj < j1);
-        P.page = *page_entry_ptr<LIST>(p, b, P.k, P.slot);
+        if constexpr (LIST == KEYS_DENSE) {
+            P.page = 0;                            // dense: no page table
+            P.slot = 0;
+        } else {
+            P.page = *page_entry_ptr<LIST>(p, b, P.k, P.slot);
+        }
     };
     auto load_rows = [&](const Pages &P, Rows &R) {
         bool ok;
@@ -381,6 +394,7 @@ int launch_gather_mfma(const GatherParams &p, void *stream)
     case KEYS_TOKEN_INDICES: return launch_mfma_t<KEYS_TOKEN_INDICES>(p, stream);
     case KEYS_BLOCKS: return launch_mfma_t<KEYS_BLOCKS>(p, stream);
     case KEYS_LATENT: return launch_mfma_t<KEYS_LATENT>(p, stream);
+    case KEYS_DENSE: return launch_mfma_t<KEYS_DENSE>(p, stream);
     default: return (int)hipErrorInvalidValue;
     }
 }

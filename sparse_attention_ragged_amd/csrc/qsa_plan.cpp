@@ -152,13 +152,17 @@ qsa_status plan_gather(const qsa_ragged_q *q, int64_t num_kv_heads, int32_t dtyp
     plan->ws_ctr_offset = 0;
     const int64_t cap = key_capacity > 0 ? key_capacity : 1;
 
+    if (list_kind == KEYS_DENSE && o.schedule == QSA_SCHEDULE_DYNAMIC) {
+        return fail(QSA_ERR_UNSUPPORTED, "the dynamic schedule does not take dense attention");
+    }
+
     // Dynamic schedule (wavefront kernel, one kv head per workgroup), on request only:
     // every (row, kv head) list is cut into units of a few key batches and a persistent
     // grid takes them from a counter. It evens out the uneven finish of static shares,
     // but measured slower than the static schedule on the decode workloads (it keeps
     // seven streaming wavefronts per CU instead of eight and merges per unit), so the
     // automatic choice is the static schedule.
-    if (plan->path == PATH_VALU && o.schedule == QSA_SCHEDULE_DYNAMIC) {
+    if (plan->path == PATH_VALU && o.schedule == QSA_SCHEDULE_DYNAMIC && list_kind != KEYS_DENSE) {
         const int eb = dtype == QSA_F32 ? 4 : dtype == QSA_BF16 ? 2 : 1;
         const int64_t per_batch = (int64_t)kDynUnitWaves * (64 / valu_team_lanes(eb, Dh)) * 2;
         int64_t bpu = kDynBatchesPerUnit;

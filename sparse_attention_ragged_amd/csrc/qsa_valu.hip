@@ -70,7 +70,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParam
     const int NK = NW * KPW;                     // key slots per workgroup
 
     // prologue: list length and the q rows go out together
-    const int64_t n = key_list_length(p, r);
+    int64_t n = LIST == KEYS_DENSE ? 0 : key_list_length(p, r);
     const char *qbase = static_cast<const char *>(p.q) + ((r * p.num_q_heads + (int64_t)g * G) * D) * EB;
     typename Core::Q q;
 #pragma unroll
@@ -79,14 +79,19 @@ __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParam
         for (int c = 0; c < CPL; ++c)
             q.raw[h][c] = ldg16(qbase + ((int64_t)h * D + Core::chunk_elem(c, ln)) * EB);
     int64_t pos = 0;
-    const int b = find_seq_pos_wave(p.row_off, LIST == KEYS_TOKEN_INDICES ? nullptr : p.cache_lengths, p.batch,
-                                    (uint32_t)r, pos);
+    const int b = find_seq_pos_wave(p.row_off,
+                                    LIST == KEYS_TOKEN_INDICES || LIST == KEYS_DENSE ? nullptr : p.cache_lengths,
+                                    p.batch, (uint32_t)r, pos);
+    if constexpr (LIST == KEYS_DENSE)
+        n = dense_key_range(p, r, b, pos);     // pos: row index of the row's first key
     const int64_t j0 = (int64_t)s * p.split_keys;
     const int64_t jend = j0 + p.split_keys;
     const int64_t j1 = n < jend ? n : jend;
     const int64_t per_batch = (int64_t)NK * U;
     const int nb = j1 > j0 ? (int)((j1 - j0 + per_batch - 1) / per_batch) : 0;
-    const int64_t vdelta = LIST == KEYS_LATENT ? 0 : (int64_t)p.kv.plane_stride_b;
+    const int64_t vdelta = LIST == KEYS_LATENT  ? 0
+                           : LIST == KEYS_DENSE ? static_cast<const char *>(p.dense_v) - static_cast<const char *>(p.dense_k)
+                                                : (int64_t)p.kv.plane_stride_b;
     const char *dummy = qbase;                   // a readable row for absent keys
 
     Core::widen_q(q);
@@ -105,7 +110,10 @@ __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParam
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t jj = key_index(batch, u);
-            E.raw[u] = *entry_ptr<LIST>(p, r, g, jj, jj < j1);
+            if constexpr (LIST == KEYS_DENSE)
+                E.raw[u] = 0;                      // dense: the key is its index, nothing to load
+            else
+                E.raw[u] = *entry_ptr<LIST>(p, r, g, jj, jj < j1);
         }
     };
     auto load_pages = [&](int batch, const Entries &E, Pages &P) {
@@ -113,7 +121,12 @@ __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParam
         for (int u = 0; u < U; ++u) {
             const int64_t jj = key_index(batch, u);
             P.k[u] = key_pos<LIST>(p, pos, jj, E.raw[u], jj < j1);
-            P.page[u] = *page_entry_ptr<LIST>(p, b, P.k[u], P.slot[u]);
+            if constexpr (LIST == KEYS_DENSE) {
+                P.page[u] = 0;                     // dense: no page table
+                P.slot[u] = 0;
+            } else {
+                P.page[u] = *page_entry_ptr<LIST>(p, b, P.k[u], P.slot[u]);
+            }
         }
     };
     auto load_rows = [&](const Pages &P, Rows &R) {
@@ -309,6 +322,7 @@ int launch_gather_valu(const GatherParams &p, void *stream)
     case KEYS_TOKEN_INDICES: return launch_valu_t<KEYS_TOKEN_INDICES>(p, stream);
     case KEYS_BLOCKS: return launch_valu_t<KEYS_BLOCKS>(p, stream);
     case KEYS_LATENT: return launch_valu_t<KEYS_LATENT>(p, stream);
+    case KEYS_DENSE: return launch_valu_t<KEYS_DENSE>(p, stream);
     default: return (int)hipErrorInvalidValue;
     }
 }

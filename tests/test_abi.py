@@ -157,6 +157,33 @@ def test_bad_launch_options(qsa, opts):
     assert call_qsa(qsa, opts=qsa.LaunchOptions(*opts)) == 4, msg(qsa)
 
 
+def test_ragged_attention_checks(qsa):
+    """Dense ragged attention: every bad argument is refused on the host, before any launch."""
+    f = qsa.lib.qsa_ragged_attention
+
+    def call(q=None, hkv=2, causal=1, window=-1, opts=None, k=P, v=P, out=P, scale=0.1):
+        q = q or ragged()
+        return f(out, 1, ctypes.byref(q), k, v, hkv, causal, window, scale,
+                 ctypes.byref(opts) if opts else None, None, 0, None)
+
+    assert call(causal=2) == 2                          # causal is 0 or 1
+    assert call(window=0) == 2 and call(window=-3) == 2   # -1 (none) or >= 1
+    assert call(hkv=3) == 2                             # 8 q heads not a multiple of 3
+    assert call(hkv=0) == 2
+    assert call(q=ragged(num_q_heads=48), hkv=2) == 4   # group 24 not built here
+    assert call(q=ragged(head_dim=96)) == 4             # head_dim 96 not built
+    assert call(q=ragged(max_prompt_length=0)) == 2     # the split plan needs the longest sequence
+    assert call(k=0) == 1 and call(v=0) == 1 and call(out=0) == 1
+    assert call(k=P + 4) == 2                           # 16-byte alignment
+    assert call(scale=float("nan")) == 2
+    assert call(opts=qsa.LaunchOptions(0, 0, 0, 2)) == 4 and "dynamic" in msg(qsa)
+    n = ctypes.c_size_t(7)
+    assert qsa.lib.qsa_ragged_attention_workspace_size(ctypes.byref(ragged()), 2, 1, -1, None,
+                                                       ctypes.byref(n)) == 0
+    assert qsa.lib.qsa_ragged_attention_workspace_size(ctypes.byref(ragged()), 2, 5, -1, None,
+                                                       ctypes.byref(n)) == 2 and n.value == 0
+
+
 def test_block_sparse_checks(qsa):
     q, kv = ragged(), cache()
     f = qsa.lib.qsa_block_sparse_attention

@@ -43,12 +43,17 @@ class DeviceCase:
     d_indices: Optional[torch.Tensor] = None
     comp_indices: Optional[torch.Tensor] = None
     attn_sink: Optional[torch.Tensor] = None
+    k: Optional[torch.Tensor] = None
+    v: Optional[torch.Tensor] = None
 
 
 def to_device(case, device="cuda") -> DeviceCase:
     dc = DeviceCase(case=case, q=case.q.to(device), row_off=_i32(case.input_row_offsets, device),
-                    kv=_leaf(case.kv, device))
-    if case.kind == "qsa":
+                    kv=_leaf(case.kv, device) if case.kv is not None else None)
+    if case.kind == "dense":
+        dc.k = case.k.to(device).contiguous()
+        dc.v = case.v.to(device).contiguous()
+    elif case.kind == "qsa":
         dc.token_indices = _i32(case.token_indices, device)
         dc.counts = _i32(case.counts, device)
     elif case.kind == "block_sparse":
@@ -72,6 +77,10 @@ def run(dc: DeviceCase, options=None, out=None, workspace=None, stream=None) -> 
         return qsa.sparse_attention(dc.q, dc.row_off, dc.kv, c.layer_idx, dc.token_indices, dc.counts,
                                     c.scale, out_dtype=out_dtype(c), max_prompt_length=c.max_prompt_length,
                                     options=options, out=out, workspace=workspace, stream=stream)
+    if c.kind == "dense":
+        return qsa.ragged_attention(dc.q, dc.k, dc.v, dc.row_off, c.scale, causal=c.causal, window=c.window,
+                                    out_dtype=out_dtype(c), max_prompt_length=c.max_prompt_length,
+                                    options=options, out=out, workspace=workspace, stream=stream)
     if c.kind == "block_sparse":
         return qsa.block_sparse_attention(dc.q, dc.row_off, dc.kv, c.layer_idx, dc.d_indices,
                                           c.block_size, c.scale, max_prompt_length=c.max_prompt_length,
@@ -88,6 +97,9 @@ def workspace_size(dc: DeviceCase, options=None) -> int:
     if c.kind == "qsa":
         return qsa.sparse_attention_workspace_size(dc.q, dc.row_off, dc.kv, dc.token_indices.shape[1],
                                                    options)
+    if c.kind == "dense":
+        return qsa.ragged_attention_workspace_size(dc.q, dc.row_off, dc.k.shape[1], c.causal, c.window,
+                                                   c.max_prompt_length, options)
     if c.kind == "block_sparse":
         return qsa.block_sparse_attention_workspace_size(dc.q, dc.row_off, dc.kv, dc.d_indices.shape[2],
                                                          c.block_size, options)
