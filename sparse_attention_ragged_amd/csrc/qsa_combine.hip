@@ -30,9 +30,12 @@ __global__ void __launch_bounds__(256) splitk_combine_kernel(GatherParams p)
         return;
     const int S = p.num_splits;
     float M = kNoKey;
+    // unrolled so that several partials' loads are in flight at once
+#pragma unroll 8
     for (int s = 0; s < S; ++s)
         M = fmaxf(M, p.ws_ml[((int64_t)s * RH + rh) * 2]);
     float L = 0.f, a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll 8
     for (int s = 0; s < S; ++s) {
         const int64_t srh = (int64_t)s * RH + rh;
         const float c = __builtin_amdgcn_exp2f(p.ws_ml[srh * 2] - M);
