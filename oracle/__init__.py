@@ -1,5 +1,6 @@
 """fp64 CPU oracle for index-selected sparse attention over a paged KV cache (and for
-dense ragged attention without a cache, the comparison row).
+dense ragged attention without a cache, the comparison row, and for the key
+compression that produces the block keys).
 
 TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package. The product library
@@ -12,7 +13,9 @@ only marshals numpy / torch-CPU arrays into it.
 
 Every function is pinned by ``tests/test_oracle_pins.py``; none is "parity
 unpinned" except where that file says so (the GQA head-to-kv-head mapping and the
-latent key-equals-value reading are conventions that no page value fixes).
+latent key-equals-value reading are conventions that no page value fixes; so are the
+key-compression choices of pooling operator, step order, rotation pairing and
+rotation position, which the pins check as stated but the pages do not fix).
 """
 from __future__ import annotations
 
@@ -69,7 +72,10 @@ def load(path: str = None):
                                    P, I64, I64, I64, I64, P, I64,
                                    I64, I64, P, I64, P, F, I]
         lib.orc_dense.argtypes = [P, P, I64, P, P, P, I, I64, I64, I64, I64, P, I64, I, I64, F, I]
-        for f in (lib.orc_decode, lib.orc_qsa, lib.orc_block_sparse, lib.orc_latent, lib.orc_dense):
+        lib.orc_compress.argtypes = [P, P, I, I64, I64, I64, I64, I64, I64, P, I64, I64, P, I64, I64, I64,
+                                     P, P, I, I64, I64, F, I]
+        for f in (lib.orc_decode, lib.orc_qsa, lib.orc_block_sparse, lib.orc_latent, lib.orc_dense,
+                  lib.orc_compress):
             f.restype = I
         _libs[path] = lib
     return _libs[path]
@@ -217,6 +223,26 @@ def dense_attention(*, q, k, v, dtype, input_row_offsets, causal, window, scale,
     return out
 
 
+def compress_keys(*, kv_blocks, dtype, num_pages, num_planes, num_layers, page_size, head_dim, page_stride,
+                  kv_lookup_table, layer_idx, key_counts, max_blocks, ratio, gamma, freqs_cis, freq_dtype,
+                  rotary_dim, eps, nthreads=None, lib=None) -> np.ndarray:
+    """Block keys pooled from raw index keys ("QSACompressKeysPaged"); fp64
+    [batch * max_blocks, head_dim], NaN in the rows past each sequence's block count."""
+    lib = lib or load()
+    keep = _Keep()
+    lut = np.asarray(kv_lookup_table, np.uint32)
+    kc = np.asarray(key_counts, np.int32)
+    batch = len(kc)
+    out = np.empty((batch * max_blocks, head_dim), np.float64)
+    npos = freqs_cis.shape[0]
+    rc = lib.orc_compress(out.ctypes.data, keep.ptr(kv_blocks), DT[dtype], num_pages, num_planes, num_layers,
+                          page_size, head_dim, page_stride, keep.ptr(lut), lut.shape[1], layer_idx, keep.ptr(kc),
+                          batch, max_blocks, ratio, keep.ptr(gamma), keep.ptr(freqs_cis), DT[freq_dtype], npos,
+                          rotary_dim, eps, nthreads or default_threads())
+    _check(rc, "orc_compress")
+    return out
+
+
 def _leaf(c):
     return dict(blocks=c.storage, num_pages=c.num_pages, num_layers=c.num_layers,
                 page_size=c.page_size, num_kv_heads=c.num_kv_heads, page_stride=c.page_stride,
@@ -251,6 +277,14 @@ def run_case(case, rows=None, nthreads=None, lib=None) -> np.ndarray:
                                        window=case.window, comp_indices=case.comp_indices,
                                        attn_sink=case.attn_sink, scale=case.scale, rows=rows,
                                        nthreads=nthreads, lib=lib)
+    if case.kind == "compress":
+        kv = case.kv
+        return compress_keys(kv_blocks=kv.storage, dtype=case.dtype, num_pages=kv.num_pages, num_planes=kv.planes,
+                             num_layers=kv.num_layers, page_size=kv.page_size, head_dim=kv.head_dim,
+                             page_stride=kv.page_stride, kv_lookup_table=kv.lookup_table,
+                             layer_idx=case.layer_idx, key_counts=case.key_counts, max_blocks=case.max_blocks,
+                             ratio=case.ratio, gamma=case.gamma, freqs_cis=case.freqs, freq_dtype=case.freq_dtype,
+                             rotary_dim=case.rotary_dim, eps=case.eps, nthreads=nthreads, lib=lib)
     if case.kind == "dense":
         return dense_attention(q=case.q, k=case.k, v=case.v, dtype=case.dtype,
                                input_row_offsets=case.input_row_offsets, causal=case.causal,

@@ -25,9 +25,13 @@
  *     (window keys max(0, pos-window+1)..pos, listed compressed entries with -1
  *     marking an unused slot, per-head sink logits, scale applied to scores).
  *
-   - "RaggedFlashAttentionGPU": summary, Parameters and Args (ragged q, k, v
+ *   - "RaggedFlashAttentionGPU": summary, Parameters and Args (ragged q, k, v
  *     [total_seq_len, heads, head_dim] without a KV cache, input_row_offsets,
  *     a mask type and an optional local window size, -1 for none).
+ *   - "QSACompressKeysPaged": summary, Tensor shapes, execute Parameters and Args
+ *     (block_keys [batch * max_blocks, head_dim], gamma [head_dim], freqs_cis
+ *     [positions, rotary_dim] of cos/sin pairs, key_counts = raw keys per sequence
+ *     this step included, ratio, rotary_dim, eps).
  *
  * Readings where the pages are silent (listed in the design notes of the repo):
  *   - query head h reads kv head h / group (consecutive groups);
@@ -39,7 +43,13 @@
  *   - dense ragged attention: row i of a sequence (0-based within it) sees the
  *     keys j of its own sequence with j <= i under the causal mask (all j of the
  *     sequence without a mask) and, with a local window w > 0, j >= i - w + 1;
- *     k and v may have fewer heads than q (query head h reads kv head h / group).
+ *     k and v may have fewer heads than q (query head h reads kv head h / group);
+ *   - key compression (parity unpinned for these choices: no page value fixes them):
+ *     the pooling is the mean of a complete group of `ratio` consecutive raw keys (a
+ *     trailing partial group gives no block key); the order is pool, then RMS-norm
+ *     with gamma, then rotation; the rotation turns interleaved channel pairs
+ *     (2i, 2i+1) below rotary_dim by the table's (cos, sin) pair at the block's first
+ *     raw position j * ratio; raw keys sit in plane 0 (K) of the indexer cache.
  *
  * Parity pins: every function here is pinned by tests/test_oracle_pins.py
  * (closed forms, invariants, brute-force dense masked attention, exhaustive
@@ -480,6 +490,87 @@ int orc_dense(double *out, const int64_t *rows, int64_t n_rows,
         free(V);
         free(s);
         free(qv);
+    }
+    return err;
+}
+
+/* ---------------------------------------------------------- key compression */
+
+/* Block keys pooled from raw index keys ("QSACompressKeysPaged": summary, Tensor
+ * shapes, execute Parameters and Args). Sequence b holds key_counts[b] raw keys at
+ * positions 0.. of plane 0, kv head 0 of the indexer cache; its complete groups of
+ * `ratio` consecutive keys become n_b = min(key_counts[b] / ratio, max_blocks) block
+ * keys, block j covering positions j*ratio .. j*ratio + ratio - 1. For block j:
+ *   pooled_d = (1 / ratio) * sum_t K[j*ratio + t]_d                 (mean pool)
+ *   normed_d = gamma_d * pooled_d / sqrt((1 / D) * sum_e pooled_e^2 + eps)
+ *   with c = F[j*ratio][2i], s = F[j*ratio][2i + 1] for each channel pair with
+ *   2i + 1 < rotary_dim, the pair turns by the angle whose cosine and sine those are:
+ *   out_2i = c * normed_2i - s * normed_2i+1, out_2i+1 = s * normed_2i + c * normed_2i+1;
+ *   channels at or past rotary_dim keep normed_d.
+ * Output rows b * max_blocks + j for j >= n_b are not produced: they are NaN here. */
+int orc_compress(double *out, const void *blocks, int dt, int64_t num_pages, int64_t planes,
+                 int64_t num_layers, int64_t page_size, int64_t D, int64_t page_stride,
+                 const uint32_t *lut, int64_t max_pages, int64_t layer_idx, const int32_t *key_counts,
+                 int64_t batch, int64_t max_blocks, int64_t ratio, const void *gamma,
+                 const void *freqs, int fdt, int64_t num_positions, int64_t rotary_dim, float eps,
+                 int nthreads)
+{
+    if (ratio < 1 || max_blocks < 0 || rotary_dim < 0 || rotary_dim % 2 || rotary_dim > D ||
+        layer_idx < 0 || layer_idx >= num_layers)
+        return ORC_EINPUT;
+    orc_cache c = {blocks, dt, num_pages, planes, num_layers, page_size, 1, D,
+                   page_stride, lut, max_pages, NULL};
+    for (int64_t i = 0; i < batch * max_blocks * D; ++i)
+        out[i] = NAN;
+    int err = ORC_OK;
+#pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1)
+    {
+        double *row = malloc(sizeof(double) * D);
+        double *x = malloc(sizeof(double) * D);
+        if (!row || !x) {
+#pragma omp atomic write
+            err = ORC_ENOMEM;
+        }
+#pragma omp for collapse(2) schedule(dynamic, 64)
+        for (int64_t b = 0; b < batch; ++b)
+            for (int64_t j = 0; j < max_blocks; ++j) {
+                int64_t nb = key_counts[b] > 0 ? key_counts[b] / ratio : 0;
+                if (err || j >= nb)
+                    continue;
+                for (int64_t d = 0; d < D; ++d)
+                    x[d] = 0.0;
+                int bad = 0;
+                for (int64_t t = 0; t < ratio; ++t) {
+                    bad |= gather_row(&c, b, j * ratio + t, 0, layer_idx, 0, row);
+                    for (int64_t d = 0; d < D; ++d)
+                        x[d] += row[d];
+                }
+                int64_t p = j * ratio;
+                if (bad || (rotary_dim > 0 && p >= num_positions)) {
+#pragma omp atomic write
+                    err = ORC_EINPUT;
+                    continue;
+                }
+                for (int64_t d = 0; d < D; ++d)
+                    x[d] /= (double)ratio;
+                double ss = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    ss += x[d] * x[d];
+                double inv = 1.0 / sqrt(ss / (double)D + (double)eps);
+                for (int64_t d = 0; d < D; ++d)
+                    x[d] = elem(gamma, dt, d) * x[d] * inv;
+                double *o = out + (b * max_blocks + j) * D;
+                for (int64_t d = 0; d < D; ++d)
+                    o[d] = x[d];
+                for (int64_t i = 0; 2 * i + 1 < rotary_dim; ++i) {
+                    double cs = elem(freqs, fdt, p * rotary_dim + 2 * i);
+                    double sn = elem(freqs, fdt, p * rotary_dim + 2 * i + 1);
+                    o[2 * i] = cs * x[2 * i] - sn * x[2 * i + 1];
+                    o[2 * i + 1] = sn * x[2 * i] + cs * x[2 * i + 1];
+                }
+            }
+        free(row);
+        free(x);
     }
     return err;
 }

@@ -628,4 +628,147 @@ def pin_dense_first_row_and_unit_window_are_v_rows(lib):
             assert_close(got[r, h], v[r, h // G], 0.0, "window 1 row %d head %d" % (r, h))
 
 
+# ------------------------------------------------------------------ pins: key compression
+
+def small_compress_case(seed=41, dtype="bf16", freq_dtype="f32", ratio=4, rotary_dim=8, D=16, eps=1e-6,
+                        cache_lengths=(13, 30, 0, 7), rows=(3, 1, 2, 1), **kw):
+    return W.make_compress(name="compress_pin", seed=seed, cache_lengths=list(cache_lengths), rows=list(rows),
+                           page_size=8, num_layers=2, layer_idx=1, head_dim=D, dtype=dtype,
+                           freq_dtype=freq_dtype, ratio=ratio, rotary_dim=rotary_dim, eps=eps, **kw)
+
+
+def torch_compress(case) -> np.ndarray:
+    """The block keys from library routines, in float64: raw keys de-paged with torch
+    indexing, each complete group averaged by Tensor.mean, torch's rms_norm with gamma,
+    and the rotation as a product of complex numbers (view_as_complex). Rows past a
+    sequence's block count are NaN, as in the oracle."""
+    D, R, rd, mb = case.head_dim, case.ratio, case.rotary_dim, case.max_blocks
+    out = np.full((case.batch * mb, D), np.nan)
+    g = case.gamma.to(torch.float32).to(torch.float64)
+    for b, nb in enumerate(case.blocks_per_sequence()):
+        nb = int(nb)
+        if nb == 0:
+            continue
+        K = torch.from_numpy(dense_keys(case.kv, b, case.layer_idx, nb * R)[0, :, 0, :])
+        x = K.reshape(nb, R, D).mean(dim=1)
+        y = torch.nn.functional.rms_norm(x, (D,), weight=g, eps=case.eps)
+        if rd:
+            f = case.freqs.to(torch.float32).to(torch.float64)[torch.arange(nb) * R]
+            z = torch.view_as_complex(y[:, :rd].reshape(nb, rd // 2, 2).contiguous()) * \
+                torch.view_as_complex(f.reshape(nb, rd // 2, 2).contiguous())
+            y = torch.cat([torch.view_as_real(z).reshape(nb, rd), y[:, rd:]], dim=1)
+        out[b * mb:b * mb + nb] = y.numpy()
+    return out
+
+
+def assert_same_rows(got, ref, tol, what):
+    """Equal NaN pattern (rows not produced) and close values elsewhere."""
+    got, ref = np.asarray(got), np.asarray(ref)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), what + ": rows produced differ"
+    live = ~np.isnan(ref)
+    err = np.abs(got[live] - ref[live]).max() if live.any() else 0.0
+    assert err <= tol, "%s: max abs diff %.3e > %.1e" % (what, err, tol)
+
+
+def pin_compress_matches_library_pipeline(lib):
+    cases = [
+        small_compress_case(),
+        small_compress_case(seed=42, dtype="f32", freq_dtype="bf16", ratio=3, rotary_dim=16),
+        small_compress_case(seed=43, ratio=1, rotary_dim=0, eps=0.5),
+        small_compress_case(seed=44, dtype="f32", ratio=5, rotary_dim=6, D=32, page_pad=3,
+                            cache_lengths=(40, 9, 22), rows=(1, 1, 4)),
+        small_compress_case(seed=45, ratio=8, rotary_dim=16, max_blocks=3),     # capped block count
+    ]
+    for case in cases:
+        assert_same_rows(oracle.run_case(case, lib=lib), torch_compress(case), 1e-12,
+                         "compress %s ratio=%d rd=%d" % (case.dtype, case.ratio, case.rotary_dim))
+
+
+def pin_compress_closed_form(lib):
+    """Hand-derived case, D 4, ratio 2, rotary 2, eps 0.5, gamma (2, 1, 0.5, 1): the two
+    raw keys of each block are u + e and u - e with u = (3, 0, 1, -1), so the mean is u,
+    mean(u^2) + eps = 11/4 + 1/2 = 13/4, and the normed key is gamma * u * 2/sqrt(13) =
+    (6, 0, 0.5, -1) * 2/sqrt(13). The table row p holds (cos, sin) of 0.1 * (p + 1), and
+    block j uses row 2j: the first pair (6k, 0) turns into (6k cos, 6k sin) of that angle;
+    channels 2 and 3 are not rotated."""
+    case = small_compress_case(seed=46, dtype="f32", ratio=2, rotary_dim=2, D=4, eps=0.5,
+                               cache_lengths=(5,), rows=(1,))
+    u = np.array([3.0, 0.0, 1.0, -1.0])
+    e = np.array([1.0, 2.0, -0.5, 0.25])
+    pv = case.kv.pages_view()
+    for p in range(6):
+        val = u + e if p % 2 == 0 else u - e
+        pv[int(case.kv.lookup_table[0, p // case.kv.page_size]), 0, case.layer_idx, p % case.kv.page_size, 0] = \
+            torch.as_tensor(val, dtype=torch.float32)
+    case.gamma = torch.tensor([2.0, 1.0, 0.5, 1.0])
+    ang = 0.1 * (np.arange(case.freqs.shape[0]) + 1)
+    case.freqs = torch.as_tensor(np.stack([np.cos(ang), np.sin(ang)], 1), dtype=torch.float32)
+    got = oracle.run_case(case, lib=lib)
+    k = 2.0 / math.sqrt(13.0)
+    f = case.freqs.to(torch.float64).numpy()
+    for j in range(3):
+        c, s = f[2 * j]
+        assert_close(got[j], [6 * k * c, 6 * k * s, 0.5 * k, -k], 1e-12, "compress closed form block %d" % j)
+    assert np.isnan(got[3:]).all(), "compress closed form: rows past the block count"
+
+
+def pin_compress_page_permutation(lib):
+    case = small_compress_case(seed=47, page_pad=2)
+    base = oracle.run_case(case, lib=lib)
+    kv = case.kv
+    perm = np.random.default_rng(98).permutation(kv.num_pages)
+    st = kv.storage.view(kv.num_pages, kv.page_elems)
+    new = torch.empty_like(st)
+    new[torch.as_tensor(perm)] = st
+    import copy
+    kv2 = copy.copy(kv)
+    kv2.storage = new.view(-1)
+    kv2.lookup_table = perm[kv.lookup_table.astype(np.int64)].astype(np.uint32)
+    c2 = copy.copy(case)
+    c2.kv = kv2
+    got = oracle.run_case(c2, lib=lib)
+    assert np.array_equal(np.isnan(got), np.isnan(base)) and np.array_equal(got[~np.isnan(got)],
+                                                                              base[~np.isnan(base)]), \
+        "page permutation changed the block keys"
+
+
+def pin_compress_reads_complete_groups_only(lib):
+    """NaN at every position of a trailing partial group (and past the key count): the
+    produced block keys are unchanged and finite; zero and negative key counts give no
+    block key."""
+    case = small_compress_case(seed=48, ratio=4, cache_lengths=(13, 30, 5, 7), rows=(3, 1, 2, 1))
+    base = oracle.run_case(case, lib=lib)
+    import copy
+    c2 = copy.copy(case)
+    c2.kv = copy.copy(case.kv)
+    c2.kv.storage = case.kv.storage.clone()
+    pv = c2.kv.pages_view()
+    for b, nb in enumerate(case.blocks_per_sequence()):
+        for p in range(int(nb) * case.ratio, case.kv.max_pages * case.kv.page_size):
+            pv[int(c2.kv.lookup_table[b, p // case.kv.page_size]), 0, case.layer_idx, p % case.kv.page_size] = \
+                float("nan")
+    got = oracle.run_case(c2, lib=lib)
+    live = ~np.isnan(base)
+    assert live.any() and np.array_equal(np.isnan(got), ~live) and np.array_equal(got[live], base[live]), \
+        "compress read a raw key outside the complete groups"
+    c3 = copy.copy(case)
+    c3.key_counts = np.array([0, -5, 3, 4], np.int32)
+    got = oracle.run_case(c3, lib=lib).reshape(4, case.max_blocks, -1)
+    assert np.isnan(got[:3]).all() and np.isfinite(got[3, 0]).all() and np.isnan(got[3, 1:]).all(), \
+        "compress block counts from zero, negative and short key counts"
+
+
+def pin_compress_scale_invariance_without_eps(lib):
+    """With eps 0 the RMS norm cancels any common scale of the raw keys: multiplying
+    them all by 4 (exact in bf16) leaves the block keys unchanged."""
+    case = small_compress_case(seed=49, eps=0.0)
+    base = oracle.run_case(case, lib=lib)
+    import copy
+    c2 = copy.copy(case)
+    c2.kv = copy.copy(case.kv)
+    c2.kv.storage = case.kv.storage * 4
+    assert_same_rows(oracle.run_case(c2, lib=lib), base, 1e-12, "compress scale invariance")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

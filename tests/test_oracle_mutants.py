@@ -46,6 +46,19 @@ MUTANTS = [
      "K[j * D + d] = elem(k, dt, ((lo + j) * Hkv + g) * D + d);"),
     ("dense_kv_head_dropped", "V[j * D + d] = elem(v, dt, ((start + lo + j) * Hkv + g) * D + d);",
      "V[j * D + d] = elem(v, dt, ((start + lo + j) * Hkv + 0) * D + d);"),
+    ("compress_sum_not_mean", "x[d] /= (double)ratio;", "x[d] /= 1.0;"),
+    ("compress_partial_group_kept", "key_counts[b] / ratio : 0", "(key_counts[b] + ratio - 1) / ratio : 0"),
+    ("compress_eps_dropped", "sqrt(ss / (double)D + (double)eps)", "sqrt(ss / (double)D)"),
+    ("compress_rms_divisor", "sqrt(ss / (double)D + (double)eps)", "sqrt(ss / (double)(D - 1) + (double)eps)"),
+    ("compress_gamma_dropped", "x[d] = elem(gamma, dt, d) * x[d] * inv;", "x[d] = x[d] * inv;"),
+    ("compress_rotation_sign", "o[2 * i] = cs * x[2 * i] - sn * x[2 * i + 1];",
+     "o[2 * i] = cs * x[2 * i] + sn * x[2 * i + 1];"),
+    ("compress_rotation_position_is_block", "int64_t p = j * ratio;", "int64_t p = j;"),
+    ("compress_rotation_past_rotary_dim", "2 * i + 1 < rotary_dim; ++i)", "2 * i + 1 < D; ++i)"),
+    ("compress_cos_sin_swapped", "double cs = elem(freqs, fdt, p * rotary_dim + 2 * i);",
+     "double cs = elem(freqs, fdt, p * rotary_dim + 2 * i + 1);"),
+    ("compress_last_block_dropped", "for (int64_t j = 0; j < max_blocks; ++j) {",
+     "for (int64_t j = 0; j < max_blocks - 1; ++j) {"),
 ]
 
 

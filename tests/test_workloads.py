@@ -53,3 +53,19 @@ def test_block_sparse_recipe():
 def test_gathered_bytes():
     c = W.c1_tiny_fp32()
     assert W.gathered_kv_bytes(c) == int(c.counts.sum()) * 1 * 2 * 64 * 4
+
+
+def test_compress_recipe():
+    c = W.make_compress(seed=5, cache_lengths=[9, 0], rows=[1, 3], page_size=4, num_layers=2, layer_idx=0,
+                        head_dim=8, dtype="bf16", ratio=4, rotary_dim=4)
+    assert c.key_counts.tolist() == [10, 3] and c.max_blocks == 3
+    assert c.blocks_per_sequence().tolist() == [2, 0]
+    pv = c.kv.pages_view()
+    assert pv[:, 1].isnan().all() and pv[:, :, 1].isnan().all()      # V plane, other layer
+    lut = c.kv.lookup_table[0]
+    assert not pv[int(lut[2]), 0, 0, :2].isnan().any() and pv[int(lut[2]), 0, 0, 2:].isnan().all()
+    f = c.freqs.double()
+    assert c.freqs.shape == (12, 4) and torch.allclose(f[:, 0::2] ** 2 + f[:, 1::2] ** 2,
+                                                       torch.ones(12, 2, dtype=torch.float64), atol=1e-6)
+    # 2 blocks x 4 keys x 16 B + 2 written x 16 B + 2 table rows x 16 B + gamma 16 B + 2 counts + 2 lut entries
+    assert W.compress_bytes(c) == 128 + 32 + 32 + 16 + 8 + 8

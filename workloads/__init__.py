@@ -405,6 +405,79 @@ def make_latent(*, name="latent", seed, decode_positions, prefill_positions, pre
                 attn_sink=sink, meta={"comp_ratio": comp_ratio})
 
 
+# --------------------------------------------------------------------------- key compression
+
+@dataclass
+class CompressCase:
+    """One key-compression call ("QSACompressKeysPaged" Tensor shapes): raw index keys
+    in plane 0, kv head 0 of a paged indexer cache, block_keys [batch * max_blocks, D]."""
+    name: str
+    seed: int
+    dtype: str                    # keys, gamma and block_keys
+    freq_dtype: str
+    kv: PagedCache                # planes 2, num_kv_heads 1
+    layer_idx: int
+    key_counts: np.ndarray        # [batch] int32 = cache_lengths + this step's rows
+    max_blocks: int
+    ratio: int
+    rotary_dim: int
+    eps: float
+    gamma: torch.Tensor           # [D] of dtype
+    freqs: torch.Tensor           # [positions, rotary_dim] of freq_dtype: (cos, sin) pairs
+    max_prompt_length: int
+    kind: str = "compress"
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def batch(self) -> int:
+        return len(self.key_counts)
+
+    @property
+    def head_dim(self) -> int:
+        return self.kv.head_dim
+
+    def blocks_per_sequence(self) -> np.ndarray:
+        """Complete groups of ``ratio`` raw keys per sequence, capped at max_blocks."""
+        kc = np.maximum(self.key_counts.astype(np.int64), 0)
+        return np.minimum(kc // self.ratio, self.max_blocks)
+
+
+def rope_table(positions: int, rotary_dim: int, base: float = 10000.0, dtype: str = "f32") -> torch.Tensor:
+    """Rotary input table [positions, rotary_dim]: row p holds the pairs
+    (cos(p * w_i), sin(p * w_i)), w_i = base^(-2i / rotary_dim), i < rotary_dim / 2."""
+    if rotary_dim == 0:
+        return torch.zeros((positions, 0), dtype=TORCH_DTYPE[dtype])
+    w = base ** (-np.arange(0, rotary_dim, 2, dtype=np.float64) / rotary_dim)
+    ang = np.arange(positions, dtype=np.float64)[:, None] * w[None, :]
+    t = np.stack([np.cos(ang), np.sin(ang)], axis=-1).reshape(positions, rotary_dim)
+    return torch.from_numpy(t).to(torch.float32).to(TORCH_DTYPE[dtype])
+
+
+def make_compress(*, name="compress", seed, cache_lengths, rows, page_size, num_layers, layer_idx, head_dim,
+                  dtype, freq_dtype="f32", ratio, rotary_dim, eps=1e-6, max_blocks=None, spare_pages=4,
+                  page_pad=0, std=1.0, positions=None) -> CompressCase:
+    """Key-compression inputs: sequence b holds key_counts[b] = cache_lengths[b] + rows[b]
+    raw keys N(0, std^2) at positions 0.. of plane 0 of ``layer_idx``; plane 1, other
+    layers, positions past key_counts and spare pages are NaN. gamma = 1 + N(0, 0.25^2).
+    max_blocks defaults to ceil(max key_counts / ratio); the rotary table has
+    ``positions`` rows (default max_blocks * ratio)."""
+    rng = np.random.default_rng(seed)
+    cl = [int(x) for x in cache_lengths]
+    rows = [int(x) for x in rows]
+    kc = np.asarray([c + r for c, r in zip(cl, rows)], np.int32)
+    kv, _ = _make_cache(rng, dtype, 2, num_layers, page_size, 1, head_dim, [int(k) for k in kc],
+                        spare_pages, page_pad, cl)
+    _fill_cache(kv, seed, 1, std, [(0, int(k) - 1) for k in kc], layer_idx)
+    nan_fill_(kv.pages_view()[:, 1])
+    if max_blocks is None:
+        max_blocks = max(1, -(-int(kc.max()) // ratio)) if len(kc) else 1
+    gamma = (1.0 + 0.25 * _normal((head_dim,), seed, 3, 1.0, "f32")).to(TORCH_DTYPE[dtype])
+    npos = max_blocks * ratio if positions is None else positions
+    return CompressCase(name, seed, dtype, freq_dtype, kv, layer_idx, kc, int(max_blocks), int(ratio),
+                        int(rotary_dim), float(np.float32(eps)), gamma, rope_table(npos, rotary_dim, dtype=freq_dtype),
+                        max(rows) if rows else 0)
+
+
 # --------------------------------------------------------------------------- named workloads
 
 def c1_tiny_fp32(seed=1):
@@ -491,6 +564,17 @@ def c5_latent_bf16(seed=5, n_decode=16, n_prefill=4, prefill_rows=128, pos_range
                        scale=1 / math.sqrt(512))
 
 
+def f2_compress_keys_bf16(seed=9, batch=32, cache_range=(16384, 32768)):
+    """Indexer key compression at the C4 decode shapes: 32 sequences, cache lengths
+    U[16k, 32k] plus one new row each, D 128, bf16 keys / gamma / block keys, ratio 4,
+    64 rotary channels from an fp32 table, page 128, 2 layers (layer 1)."""
+    rng = np.random.default_rng(seed + 10_000)
+    cl = rng.integers(cache_range[0], cache_range[1], size=batch, endpoint=True)
+    return make_compress(name="f2_compress_keys_bf16", seed=seed, cache_lengths=cl, rows=[1] * batch,
+                         page_size=128, num_layers=2, layer_idx=1, head_dim=128, dtype="bf16", freq_dtype="f32",
+                         ratio=4, rotary_dim=64, eps=1e-6)
+
+
 NAMED = {
     "c1_tiny_fp32": c1_tiny_fp32,
     "c2_decode_bf16": c2_decode_bf16,
@@ -500,6 +584,7 @@ NAMED = {
     "c4p_block_sparse_prefill_bf16": c4p_block_sparse_prefill_bf16,
     "c5_latent_bf16": c5_latent_bf16,
     "f3_dense_prefill_bf16": f3_dense_prefill_bf16,
+    "f2_compress_keys_bf16": f2_compress_keys_bf16,
 }
 
 
@@ -530,6 +615,20 @@ def gathered_kv_bytes(case: Case) -> int:
         comp = (case.comp_indices >= 0).sum()
         return int(win + comp) * D * eb
     raise ValueError(case.kind)
+
+
+def compress_bytes(case: CompressCase) -> int:
+    """Algorithmic bytes of one key-compression call: the raw keys of every complete
+    group, the block keys written, each rotary table row used once (rows are shared
+    across sequences), gamma, the key counts and the page-table entries read."""
+    eb = ELEM_BYTES[case.dtype]
+    D = case.head_dim
+    nb = case.blocks_per_sequence()
+    keys = int(nb.sum()) * case.ratio * D * eb
+    writes = int(nb.sum()) * D * eb
+    freqs = (int(nb.max()) if len(nb) else 0) * case.rotary_dim * ELEM_BYTES[case.freq_dtype]
+    pages = int(sum(-(-int(n) * case.ratio // case.kv.page_size) for n in nb)) * 4
+    return keys + writes + freqs + D * eb + 4 * case.batch + pages
 
 
 def dense_key_counts(case: Case) -> np.ndarray:
