@@ -16,8 +16,9 @@ Prints one JSON line: throughput in gathered-KV GB/s (value), query rows/s, the
 fraction of the 8 TB/s HBM peak, a roofline object for the gather kernel timed with
 HIP events around that kernel alone, the fp64 CPU oracle timed on the host as a
 baseline, and the same step measurements for the other workloads (ragged prefill
-with 16 q heads per kv head, block-sparse e4m3 top-16 decode, latent window +
-compressed + sink) under "other_workloads".
+with 16 q heads per kv head, block-sparse e4m3 top-16 decode and speculative decode,
+latent window + compressed + sink, dense causal prefill without a cache, and the key
+compression that produces the block keys) under "other_workloads".
 """
 from __future__ import annotations
 
@@ -40,14 +41,20 @@ HBM_PEAK_GBPS = 8000.0
 COUNTERS_SUMMARY = os.path.join(ROOT, "profiles", "gather_valu_c2_decode_bf16_counters.md")
 
 
+# The sources that build and plan the C2 gather kernel (its translation unit with the
+# headers it includes, and the planner that picks its launch): the committed counter
+# summary applies while these hash to the value stored with it.
+GATHER_SOURCES = ("sparse_attention_ragged_amd/csrc/qsa_valu.hip", "sparse_attention_ragged_amd/csrc/qsa_valu_core.hpp",
+                  "sparse_attention_ragged_amd/csrc/qsa_device.hpp", "sparse_attention_ragged_amd/csrc/qsa_host.hpp",
+                  "sparse_attention_ragged_amd/csrc/qsa_plan.cpp", "include/qsa.h")
+
+
 def csrc_digest():
-    """sha256 over the library's kernel and host sources (names and contents, sorted)."""
-    d = os.path.join(ROOT, "sparse_attention_ragged_amd", "csrc")
+    """sha256 over the gather kernel's sources (names and contents, in a fixed order)."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(d)):
-        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
-            h.update(name.encode())
-            h.update(open(os.path.join(d, name), "rb").read())
+    for name in GATHER_SOURCES:
+        h.update(name.encode())
+        h.update(open(os.path.join(ROOT, name), "rb").read())
     return h.hexdigest()
 
 
@@ -179,14 +186,19 @@ def time_steps(calls, opts, out, ws, stream, steps, warmup):
     """Milliseconds per step over `steps` back-to-back calls (step k uses calls[k % R]),
     then the gather kernel's average milliseconds from the HIP events the library
     records around it, over a second pass of `steps` calls."""
-    import torch
-    import sparse_attention_ragged_amd as qsa
     from workloads import device as D
     R = len(calls)
 
     def step(k):
         D.run(calls[k % R], options=opts, out=out, workspace=ws, stream=stream)
 
+    return time_step_fn(step, steps, warmup)
+
+
+def time_step_fn(step, steps, warmup):
+    """time_steps for any step(k) callable that makes one library call."""
+    import torch
+    import sparse_attention_ragged_amd as qsa
     for k in range(warmup):
         step(k)
     torch.cuda.synchronize()
@@ -235,6 +247,46 @@ def other_workload(name, make, R, dev, stream, steps, warmup):
            "unit_of_work": a["unit"], "units_per_launch": a["units"],
            "parity_max_abs_sampled_rows": sampled_parity(case, out)}
     del calls, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def compress_workload(name, make, R, dev, stream, steps, warmup):
+    """Key compression (the step that produces the block keys): raw index keys read once,
+    block keys written once; the indexer pool is replicated R times."""
+    import numpy as np
+    import torch
+    import oracle
+    import workloads as W
+    from workloads import device as D
+    log("%s: generating" % name)
+    case = make()
+    dc = D.compress_to_device(case, dev)
+    calls = []
+    for leaf in _replicate_leaf(dc.kv, R):
+        c = copy.copy(dc)
+        c.kv = leaf
+        calls.append(c)
+    del dc
+    out = torch.empty((case.batch * case.max_blocks, case.head_dim), dtype=W.TORCH_DTYPE[case.dtype], device=dev)
+    torch.cuda.synchronize()
+    log("%s: timing %d steps (+ %d with kernel events)" % (name, steps, steps))
+    ms_step, kern = time_step_fn(lambda k: D.run_compress(calls[k % R], out=out, stream=stream), steps, warmup)
+    nb = case.blocks_per_sequence()
+    algo = W.compress_bytes(case)
+    ref = oracle.run_case(case)
+    live = ~np.isnan(ref)
+    got = out.float().cpu().double().numpy()
+    res = {"workload": name, "sequences": case.batch, "block_keys": int(nb.sum()), "dtype": case.dtype,
+           "raw_key_bytes_per_step": int(nb.sum()) * case.ratio * case.head_dim * W.ELEM_BYTES[case.dtype],
+           "algorithmic_bytes_per_step": algo, "kv_pool_replicas": R, "steps": steps,
+           "ms_per_step": round(ms_step, 5),
+           "GBps": round(algo / (ms_step * 1e-3) / 1e9, 1),
+           "compress_kernel_avg_us": round(kern * 1e3, 2),
+           "compress_kernel_GBps": round(algo / (kern * 1e-3) / 1e9, 1),
+           "unit_of_work": "block key: ratio*D*elem raw key bytes + D*elem written (+ table, gamma, counts, page entries)",
+           "parity_max_abs_all_block_keys": float(np.abs(got[live] - ref[live]).max())}
+    del calls, out
     torch.cuda.empty_cache()
     return res
 
@@ -363,6 +415,7 @@ def main():
             other_workload("c4s_block_sparse_spec_fp8", W.c4s_block_sparse_spec_fp8, 8, dev, stream, n, 3),
             other_workload("c5_latent_bf16", W.c5_latent_bf16, 4, dev, stream, n, 3),
             other_workload("f3_dense_prefill_bf16", W.f3_dense_prefill_bf16, 1, dev, stream, n, 3),
+            compress_workload("f2_compress_keys_bf16", W.f2_compress_keys_bf16, 4, dev, stream, n, 3),
         ]
     if not args.no_cpu_baseline:
         log("cpu baseline (~%.0f s)" % args.cpu_seconds)

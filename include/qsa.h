@@ -16,6 +16,9 @@
  *                                ("latent_sparse_attention_ragged_paged", summary,
  *                                Parameters and Args).
  *
+ * and the key compression that produces the block keys block selection scores
+ * (qsa_compress_keys, "QSACompressKeysPaged").
+ *
  * Conventions shared by every entry point:
  *   - Pointers are DEVICE pointers unless a comment says (host). The caller owns
  *     every buffer; the library writes only `out` and `workspace`, never
@@ -52,7 +55,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 2
+#define QSA_ABI_VERSION 3
 
 /* Element types. QSA_FP8_E4M3 is the OCP 8-bit E4M3 "fn" format (bias 7, max 448,
  * no infinity), scale-free as the block-sparse page states for its FP8 path. */
@@ -233,6 +236,47 @@ qsa_status qsa_ragged_attention(void *out, int32_t out_dtype, const qsa_ragged_q
                                 const void *v, int64_t num_kv_heads, int32_t causal, int64_t window,
                                 float scale, const qsa_launch_options *opts, void *workspace,
                                 size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------- */
+/* Key compression ("QSACompressKeysPaged": summary, Tensor shapes, execute Parameters
+ * and Args): pools the raw index keys of a paged indexer cache into dense block keys,
+ * the keys that block selection scores.
+ *
+ * Sequence b holds key_counts[b] raw keys (cache_lengths[b] plus this step's rows) at
+ * positions 0.. of plane 0, kv head 0, layer layer_idx of `kv`. Its complete groups of
+ * `ratio` consecutive keys give n_b = min(key_counts[b] / ratio, max_blocks) block keys;
+ * block j (raw positions j*ratio .. j*ratio + ratio - 1) is
+ *   x   = the mean of the group's raw keys,
+ *   y_d = gamma_d * x_d / sqrt(mean over d of x_d^2 + eps),
+ *   and for each channel pair (2i, 2i+1) with 2i + 1 < rotary_dim, with (c, s) =
+ *   freqs_cis[j*ratio, 2i : 2i+2]: (c*y_2i - s*y_2i+1, s*y_2i + c*y_2i+1);
+ *   channels at or past rotary_dim stay y_d.
+ * (The pages name the pooling, the RMS norm and the rotary table but fix neither the
+ * pooling operator nor the order nor the pairing: these are this library's readings.)
+ * Block key j of sequence b is row b * max_blocks + j of block_keys. A trailing partial
+ * group gives no block key, and rows at or past n_b are not written (they keep what
+ * the caller left there).
+ *
+ *   block_keys    [batch * max_blocks, head_dim] of kv->dtype (F32 or BF16), 16-byte aligned
+ *   gamma         [head_dim] of kv->dtype (the key RMS-norm weight), 16-byte aligned
+ *   freqs_cis     [num_positions, rotary_dim] of freq_dtype (F32 or BF16): row p holds
+ *                 rotary_dim / 2 (cos, sin) pairs; may be NULL when rotary_dim == 0
+ *   key_counts    [batch] int32; <= 0 gives no block key
+ *   kv            num_planes == 2, num_kv_heads == 1, head_dim * element size a power
+ *                 of two in [16, 1024] bytes; kv->cache_lengths is part of the cache's
+ *                 description and not read by this operation
+ *   ratio >= 1, 0 <= rotary_dim <= head_dim (even), eps >= 0 (the pages' string eps)
+ * Launch bound: when kv->max_cache_length + max_prompt_length (host) is non-zero,
+ * blocks past (that sum) / ratio are not computed, so key_counts must not exceed it;
+ * freqs_cis must hold every position a computed block starts at (checked on the host).
+ * A block whose positions or pages do not address the cache is not written.
+ * No workspace; asynchronous on `stream`.
+ */
+qsa_status qsa_compress_keys(void *block_keys, int64_t max_blocks, const void *gamma, const void *freqs_cis,
+                             int32_t freq_dtype, int64_t num_positions, int64_t rotary_dim,
+                             const int32_t *key_counts, const qsa_paged_cache *kv, int64_t batch,
+                             uint32_t layer_idx, uint32_t max_prompt_length, int64_t ratio, float eps,
+                             void *stream);
 
 /* ------------------------------------------------------------------------- */
 /* Text describing the last non-OK status returned on the calling thread. */

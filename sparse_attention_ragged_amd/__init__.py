@@ -12,7 +12,10 @@ Entry points (same names as the C ABI, without the ``qsa_`` prefix):
 * ``block_sparse_attention`` - top-k KV blocks per (kv head, row), bf16 output
   ("Struct_msa_attention_ragged_paged");
 * ``latent_sparse_attention`` - one latent head: sliding window + listed compressed
-  entries + per-head sink ("latent_sparse_attention_ragged_paged").
+  entries + per-head sink ("latent_sparse_attention_ragged_paged");
+* ``ragged_attention`` - dense ragged attention without a cache ("RaggedFlashAttentionGPU");
+* ``compress_keys`` - block keys pooled from the raw index keys of a paged indexer
+  cache ("QSACompressKeysPaged").
 """
 from __future__ import annotations
 
@@ -37,7 +40,7 @@ EXPORTS = (
     "qsa_sparse_attention_workspace_size", "qsa_sparse_attention",
     "qsa_block_sparse_attention_workspace_size", "qsa_block_sparse_attention",
     "qsa_latent_sparse_attention_workspace_size", "qsa_latent_sparse_attention",
-    "qsa_ragged_attention_workspace_size", "qsa_ragged_attention",
+    "qsa_ragged_attention_workspace_size", "qsa_ragged_attention", "qsa_compress_keys",
     "qsa_last_error", "qsa_abi_version", "qsa_struct_size", "qsa_set_timing_events",
 )
 
@@ -93,10 +96,12 @@ def _load():
                                                 po, P, SZ, P]
     lib.qsa_ragged_attention_workspace_size.argtypes = [pr, I64, I32, I64, po, ctypes.POINTER(SZ)]
     lib.qsa_ragged_attention.argtypes = [P, I32, pr, P, P, I64, I32, I64, F, po, P, SZ, P]
+    U32 = ctypes.c_uint32
+    lib.qsa_compress_keys.argtypes = [P, I64, P, P, I32, I64, I64, P, pc, I64, U32, U32, I64, F, P]
     for name in ("qsa_sparse_attention_workspace_size", "qsa_sparse_attention",
                  "qsa_block_sparse_attention_workspace_size", "qsa_block_sparse_attention",
                  "qsa_latent_sparse_attention_workspace_size", "qsa_latent_sparse_attention",
-                 "qsa_ragged_attention_workspace_size", "qsa_ragged_attention"):
+                 "qsa_ragged_attention_workspace_size", "qsa_ragged_attention", "qsa_compress_keys"):
         getattr(lib, name).restype = ctypes.c_int
     lib.qsa_last_error.restype = ctypes.c_char_p
     lib.qsa_abi_version.restype = I32
@@ -345,6 +350,41 @@ def ragged_attention(q, k, v, input_row_offsets, scale: float, *, causal: bool =
     _check(lib.qsa_ragged_attention(
         out.data_ptr(), DTYPE_CODE[out_dtype], ctypes.byref(rq), k.data_ptr(), v.data_ptr(), k.shape[1],
         int(bool(causal)), window, scale, o, ws.data_ptr() if ws is not None else None, wsb, _stream(q, stream)))
+    return out
+
+
+def compress_keys(kv: PagedCache, key_counts, gamma, freqs_cis, layer_idx: int, ratio: int, rotary_dim: int,
+                  eps: float, *, max_blocks: int, max_prompt_length: int = 0, out=None,
+                  stream=None) -> torch.Tensor:
+    """Block keys pooled from the raw index keys in plane 0 of ``kv``; key_counts [batch]
+    int32; gamma [head_dim] of the cache dtype; freqs_cis [positions, rotary_dim] (float32
+    or bfloat16 cos/sin pairs). Returns block_keys [batch * max_blocks, head_dim]; rows
+    past a sequence's block count keep what ``out`` held (uninitialised when ``out`` is None)."""
+    _need_gpu(key_counts, gamma, freqs_cis)
+    _need_i32(key_counts)
+    dt = kv.blocks.dtype
+    if gamma.dtype != dt or gamma.numel() != kv.head_dim:
+        raise ValueError("gamma must be [head_dim] of the cache dtype")
+    if freqs_cis is not None and (freqs_cis.dim() != 2 or freqs_cis.shape[1] != rotary_dim):
+        raise ValueError("freqs_cis must be [positions, rotary_dim]")
+    batch = key_counts.numel()
+    if batch != kv.lookup_table.shape[0]:
+        raise ValueError("key_counts has %d sequences, the page table %d" % (batch, kv.lookup_table.shape[0]))
+    shape = (batch * max_blocks, kv.head_dim)
+    if out is None:
+        out = torch.empty(shape, dtype=dt, device=kv.blocks.device)
+    else:
+        _need_gpu(out)
+        if tuple(out.shape) != shape or out.dtype != dt:
+            raise ValueError("out must be %s of %s" % (shape, dt))
+    ck = kv._c()
+    have_f = freqs_cis is not None and freqs_cis.numel() > 0
+    _check(lib.qsa_compress_keys(out.data_ptr(), max_blocks, gamma.data_ptr(),
+                                 freqs_cis.data_ptr() if have_f else None,
+                                 DTYPE_CODE[freqs_cis.dtype] if freqs_cis is not None else F32,
+                                 freqs_cis.shape[0] if freqs_cis is not None else 0, rotary_dim,
+                                 key_counts.data_ptr(), ctypes.byref(ck), batch, layer_idx, max_prompt_length,
+                                 ratio, eps, _stream(kv.blocks, stream)))
     return out
 
 

@@ -1,6 +1,7 @@
 // extern "C" entry points declared in include/qsa.h: check arguments on the host,
 // plan the launch, fill the parameter block and hand it to the kernel launchers.
 // No HIP headers here; all device work goes through the launchers.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 
@@ -384,6 +385,90 @@ qsa_status qsa_ragged_attention(void *out, int32_t out_dtype, const qsa_ragged_q
     p.dense_causal = causal;
     p.window = window > 0 ? window : 0;
     return run(p, plan, stream);
+}
+
+qsa_status qsa_compress_keys(void *block_keys, int64_t max_blocks, const void *gamma, const void *freqs_cis,
+                             int32_t freq_dtype, int64_t num_positions, int64_t rotary_dim,
+                             const int32_t *key_counts, const qsa_paged_cache *kv, int64_t batch,
+                             uint32_t layer_idx, uint32_t max_prompt_length, int64_t ratio, float eps,
+                             void *stream)
+{
+    clear_error();
+    qsa_status s = check_cache(kv, "kv", 2);
+    if (s != QSA_OK)
+        return s;
+    if (kv->num_kv_heads != 1)
+        return fail(QSA_ERR_SHAPE, "the indexer cache holds one head (num_kv_heads must be 1)");
+    if (!compress_supported(kv->dtype, (int32_t)std::min<int64_t>(kv->head_dim, 1 << 20)))
+        return fail(kv->dtype == QSA_F32 || kv->dtype == QSA_BF16 ? QSA_ERR_UNSUPPORTED : QSA_ERR_DTYPE,
+                    "key compression takes F32 or BF16 keys whose rows are 16, 32, 64, ... or 1024 bytes "
+                    "(dtype %d, head_dim %lld)", kv->dtype, (long long)kv->head_dim);
+    if (layer_idx >= (uint64_t)kv->num_layers)
+        return fail(QSA_ERR_SHAPE, "layer_idx %u >= num_layers %lld", layer_idx, (long long)kv->num_layers);
+    if (batch < 0 || batch > (int64_t(1) << 31) - 1 || max_blocks < 0)
+        return fail(QSA_ERR_SHAPE, "batch and max_blocks must be >= 0 (batch < 2^31)");
+    if (ratio < 1 || ratio > (int64_t(1) << 30))
+        return fail(QSA_ERR_SHAPE, "ratio must be >= 1");
+    if (rotary_dim < 0 || rotary_dim % 2 || rotary_dim > kv->head_dim)
+        return fail(QSA_ERR_SHAPE, "rotary_dim %lld must be even and within [0, head_dim %lld]",
+                    (long long)rotary_dim, (long long)kv->head_dim);
+    if (freq_dtype != QSA_F32 && freq_dtype != QSA_BF16)
+        return fail(QSA_ERR_DTYPE, "freq_dtype must be QSA_F32 or QSA_BF16");
+    if (!std::isfinite(eps) || eps < 0.f)
+        return fail(QSA_ERR_SHAPE, "eps must be finite and >= 0");
+    // blocks per sequence the launch covers: the row stride, the keys the step can hold
+    // (max_cache_length + max_prompt_length, when given) and the positions the page
+    // table (and 31-bit positions) can address
+    int64_t bound = max_blocks;
+    const int64_t hint = (int64_t)kv->max_cache_length + (int64_t)max_prompt_length;
+    if (hint > 0)
+        bound = std::min(bound, hint / ratio);
+    const int64_t addressable = std::min(kv->max_pages * kv->page_size, (int64_t(1) << 31) - 1);
+    bound = std::min(bound, addressable / ratio);
+    if (batch == 0 || bound == 0)
+        return QSA_OK;
+    if (!block_keys || !gamma || !key_counts)
+        return fail(QSA_ERR_NULL, "block_keys, gamma and key_counts are required");
+    if (!aligned16(block_keys) || !aligned16(gamma))
+        return fail(QSA_ERR_SHAPE, "block_keys and gamma must be 16-byte aligned");
+    if (rotary_dim > 0) {
+        if (!freqs_cis)
+            return fail(QSA_ERR_NULL, "freqs_cis is required when rotary_dim > 0");
+        if (((uintptr_t)freqs_cis & (freq_dtype == QSA_F32 ? 7u : 3u)) != 0)
+            return fail(QSA_ERR_SHAPE, "freqs_cis must be aligned to one (cos, sin) pair");
+        if (num_positions < 0 || (bound - 1) * ratio >= num_positions)
+            return fail(QSA_ERR_SHAPE, "freqs_cis has %lld positions; blocks up to %lld start at position %lld",
+                        (long long)num_positions, (long long)bound, (long long)((bound - 1) * ratio));
+    }
+    const int64_t per_wg = kCompressThreads / compress_team_lanes(kv->dtype == QSA_F32 ? 4 : 2, (int)kv->head_dim);
+    if (batch * ((bound + per_wg - 1) / per_wg) > (int64_t(1) << 31) - 1)
+        return fail(QSA_ERR_SHAPE, "batch * max_blocks out of range");
+    CompressParams p;
+    std::memset(&p, 0, sizeof p);
+    p.out = block_keys;
+    p.gamma = gamma;
+    p.freqs = freqs_cis;
+    p.key_counts = key_counts;
+    p.kv = cache_addr(kv, layer_idx);
+    p.max_blocks = max_blocks;
+    p.blocks_bound = bound;
+    p.dtype = kv->dtype;
+    p.freq_dtype = freq_dtype;
+    p.head_dim = (int32_t)kv->head_dim;
+    p.rotary_dim = (int32_t)rotary_dim;
+    p.ratio = (int32_t)ratio;
+    p.batch = (int32_t)batch;
+    p.eps = eps;
+    int err = 0;
+    if (t_ev_start && t_ev_stop)
+        err = record_event(t_ev_start, stream);
+    if (!err)
+        err = launch_compress_keys(p, stream);
+    if (!err && t_ev_start && t_ev_stop)
+        err = record_event(t_ev_stop, stream);
+    if (err)
+        return fail(QSA_ERR_HIP, "HIP launch failed: %s", hip_error_text(err));
+    return QSA_OK;
 }
 
 void qsa_set_timing_events(void *start, void *stop)

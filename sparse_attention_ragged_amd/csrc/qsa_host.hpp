@@ -142,12 +142,36 @@ qsa_status plan_gather(const qsa_ragged_q *q, int64_t num_kv_heads, int32_t dtyp
                        Plan *plan);
 CacheAddr cache_addr(const qsa_paged_cache *c, uint32_t layer);
 
+// Key compression: one team of lanes per block key (qsa_compress.hip).
+struct CompressParams {
+    void *out;                   // block_keys [batch * max_blocks, head_dim], element type `dtype`
+    const void *gamma;           // [head_dim], element type `dtype`
+    const void *freqs;           // [num_positions, rotary_dim] of freq_dtype (cos, sin pairs)
+    const int32_t *key_counts;   // [batch]
+    CacheAddr kv;                // plane 0 (raw keys), kv head 0, the addressed layer
+    int64_t max_blocks;          // row stride of one sequence in `out`
+    int64_t blocks_bound;        // blocks per sequence the grid covers (host-side bound)
+    int32_t dtype;
+    int32_t freq_dtype;
+    int32_t head_dim;
+    int32_t rotary_dim;
+    int32_t ratio;
+    int32_t batch;
+    float eps;
+};
+
+// Threads of a compression workgroup, and the lanes that share one raw key row there
+// (one 16-byte chunk each).
+constexpr int kCompressThreads = 256;
+constexpr int compress_team_lanes(int elem_bytes, int head_dim) { return head_dim * elem_bytes / 16; }
+
 // Launchers (qsa_*.hip). Return a hipError_t value (0 = success).
 int launch_gather_valu(const GatherParams &p, void *stream);
 int launch_gather_valu_dyn(const GatherParams &p, void *stream);
 int launch_gather_mfma(const GatherParams &p, void *stream);
 int launch_gather_mfma_wide(const GatherParams &p, void *stream);
 int launch_splitk_combine(const GatherParams &p, void *stream);
+int launch_compress_keys(const CompressParams &p, void *stream);
 int record_event(void *event, void *stream);
 const char *hip_error_text(int err);
 
@@ -155,5 +179,6 @@ const char *hip_error_text(int err);
 bool valu_supported(int32_t dtype, int32_t group, int32_t head_dim);
 bool mfma_supported(int32_t dtype, int32_t group, int32_t head_dim);
 bool mfma_wide_supported(int32_t dtype, int32_t group, int32_t head_dim, int32_t list_kind);
+bool compress_supported(int32_t dtype, int32_t head_dim);
 
 }  // namespace qsa

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(qsa):
 
 
 def test_abi_version_and_struct_sizes(qsa):
-    assert qsa.lib.qsa_abi_version() == 2
+    assert qsa.lib.qsa_abi_version() == 3
     assert qsa.lib.qsa_struct_size(0) == ctypes.sizeof(qsa._Cache) == 104
     assert qsa.lib.qsa_struct_size(1) == ctypes.sizeof(qsa._Ragged) == 64
     assert qsa.lib.qsa_struct_size(2) == ctypes.sizeof(qsa.LaunchOptions) == 16
@@ -216,3 +216,37 @@ def test_binding_refuses_cpu_tensors(qsa):
     with pytest.raises(ValueError):
         qsa.sparse_attention(q, torch.zeros(2, dtype=torch.int32), None, 0, torch.zeros(2, 4, dtype=torch.int32),
                              torch.zeros(2, dtype=torch.int32), 0.1)
+
+
+def test_compress_keys_checks(qsa):
+    """Key compression: every bad argument is refused on the host, before any launch;
+    an empty batch or a zero block bound returns OK without launching anything."""
+    f = qsa.lib.qsa_compress_keys
+    ind = dict(num_kv_heads=1, max_cache_length=60, max_pages=4, page_size=16)
+
+    def call(kv=None, out=P, max_blocks=16, gamma=P, freqs=P, fdt=0, npos=64, rd=64, counts=P, batch=2,
+             layer=0, mpl=4, ratio=4, eps=1e-6):
+        kv = kv or cache(**ind)
+        return f(out, max_blocks, gamma, freqs, fdt, npos, rd, counts, ctypes.byref(kv), batch, layer, mpl,
+                 ratio, eps, None)
+
+    assert call(kv=cache(num_kv_heads=2)) == 2 and "one head" in msg(qsa)
+    assert call(kv=cache(dtype=2, **ind)) == 3                       # e4m3 keys are not offered
+    assert call(kv=cache(head_dim=96, **ind)) == 4                   # 192-byte rows not built
+    assert call(kv=cache(num_planes=1, **ind)) == 2                  # the indexer group has K and V planes
+    assert call(layer=2) == 2
+    assert call(ratio=0) == 2
+    assert call(rd=3) == 2 and call(rd=130) == 2 and call(rd=-2) == 2
+    assert call(fdt=2) == 3
+    assert call(eps=float("nan")) == 2 and call(eps=-1.0) == 2
+    assert call(max_blocks=-1) == 2 and call(batch=-1) == 2
+    # blocks up to min(16, (60 + 4) / 4) = 16 start at positions up to 60: the table needs 61 rows
+    assert call(npos=60) == 2 and "positions" in msg(qsa)
+    assert call(gamma=0) == 1 and call(counts=0) == 1 and call(out=0) == 1
+    assert call(freqs=0) == 1                                        # needed when rd > 0
+    assert call(out=P + 8) == 2 and call(gamma=P + 4) == 2
+    assert call(freqs=P + 2) == 2                                    # fp32 pairs are 8-byte aligned
+    # nothing to compute: OK, no launch
+    assert call(batch=0) == 0
+    assert call(max_blocks=0) == 0
+    assert call(kv=cache(num_kv_heads=1, max_cache_length=2, max_pages=4, page_size=16), mpl=1) == 0  # 3 / 4 = 0

@@ -105,3 +105,27 @@ def workspace_size(dc: DeviceCase, options=None) -> int:
                                                          c.block_size, options)
     return qsa.latent_sparse_attention_workspace_size(dc.q, dc.row_off, c.window,
                                                       dc.comp_indices.shape[1], options)
+
+
+@dataclass
+class DeviceCompress:
+    case: object
+    kv: object
+    key_counts: torch.Tensor
+    gamma: torch.Tensor
+    freqs: torch.Tensor
+
+
+def compress_to_device(case, device="cuda") -> DeviceCompress:
+    """Device copies of a ``workloads.CompressCase``."""
+    return DeviceCompress(case=case, kv=_leaf(case.kv, device), key_counts=_i32(case.key_counts, device),
+                          gamma=case.gamma.to(device).contiguous(), freqs=case.freqs.to(device).contiguous())
+
+
+def run_compress(dc: DeviceCompress, out=None, stream=None) -> torch.Tensor:
+    """One key-compression call; returns block_keys [batch * max_blocks, head_dim]."""
+    import sparse_attention_ragged_amd as qsa
+    c = dc.case
+    return qsa.compress_keys(dc.kv, dc.key_counts, dc.gamma, dc.freqs, c.layer_idx, c.ratio, c.rotary_dim, c.eps,
+                             max_blocks=c.max_blocks, max_prompt_length=c.max_prompt_length, out=out,
+                             stream=stream)
