@@ -41,6 +41,7 @@ void fill_common(GatherParams &p, void *out, int32_t out_dtype, const qsa_ragged
     p.waves = plan.waves;
     p.unroll = plan.unroll;
     p.split_keys = plan.split_keys;
+    p.split_row0 = plan.split_row0;
     p.head_block = plan.head_block;
     if (plan.num_splits > 1 || plan.schedule == SCHED_DYNAMIC) {
         p.ws_acc = static_cast<float *>(ws);

@@ -21,23 +21,26 @@ __global__ void __launch_bounds__(256) splitk_combine_kernel(GatherParams p)
     const int D = p.head_dim;
     const int tpr = D / 4;                     // threads per (row, head), 4 values each
     const int per_block = 256 / tpr;
-    const int64_t RH = p.total_q * p.num_q_heads;
-    const int64_t rh = (int64_t)blockIdx.x * per_block + threadIdx.x / tpr;
+    // partials exist for the rows from split_row0 on (all rows unless a tail plan ran
+    // the earlier ones unsplit); they are indexed relative to that row
+    const int64_t RH = (p.total_q - p.split_row0) * p.num_q_heads;
+    const int64_t rel = (int64_t)blockIdx.x * per_block + threadIdx.x / tpr;
+    const int64_t rh = p.split_row0 * p.num_q_heads + rel;
     const int d0 = (threadIdx.x % tpr) * 4;
     if (p.sched_counter && blockIdx.x == 0 && threadIdx.x == 0)
         *p.sched_counter = 0u;
-    if (rh >= RH || threadIdx.x / tpr >= per_block)
+    if (rel >= RH || threadIdx.x / tpr >= per_block)
         return;
     const int S = p.num_splits;
     float M = kNoKey;
     // unrolled so that several partials' loads are in flight at once
 #pragma unroll 8
     for (int s = 0; s < S; ++s)
-        M = fmaxf(M, p.ws_ml[((int64_t)s * RH + rh) * 2]);
+        M = fmaxf(M, p.ws_ml[((int64_t)s * RH + rel) * 2]);
     float L = 0.f, a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll 8
     for (int s = 0; s < S; ++s) {
-        const int64_t srh = (int64_t)s * RH + rh;
+        const int64_t srh = (int64_t)s * RH + rel;
         const float c = __builtin_amdgcn_exp2f(p.ws_ml[srh * 2] - M);
         L += c * p.ws_ml[srh * 2 + 1];
         const float4 v = *reinterpret_cast<const float4 *>(p.ws_acc + srh * D + d0);
@@ -58,7 +61,7 @@ __global__ void __launch_bounds__(256) splitk_combine_kernel(GatherParams p)
 
 int launch_splitk_combine(const GatherParams &p, void *stream)
 {
-    const int64_t RH = p.total_q * p.num_q_heads;
+    const int64_t RH = (p.total_q - p.split_row0) * p.num_q_heads;
     if (RH == 0)
         return 0;
     if (p.head_dim % 4 != 0 || p.head_dim / 4 > 256)

@@ -80,6 +80,7 @@ struct GatherParams {
     int32_t waves;
     int32_t unroll;
     int64_t split_keys;              // keys per split (in key-list units)
+    int64_t split_row0;              // rows before it run unsplit (head-split kernel's tail plan)
     int32_t head_block;              // wavefront kernel: kv heads one workgroup covers
     float *ws_acc;                   // [S, total_q, Hq, D] when num_splits > 1 or scheduled
     float *ws_ml;                    // [S, total_q, Hq, 2]
@@ -106,6 +107,7 @@ struct Plan {
     int32_t unroll;
     int64_t key_capacity;   // upper bound of keys per (row, kv head)
     int64_t split_keys;
+    int64_t split_row0;     // rows before it run unsplit; the rest num_splits ways (0: all rows)
     int32_t head_block;     // wavefront kernel: kv heads per workgroup (1 for other paths)
     int32_t schedule;       // Schedule
     int32_t sched_bpu;      // SCHED_DYNAMIC: key batches per unit

@@ -79,10 +79,15 @@ gather_mfma_wide_kernel(GatherParams p)
     constexpr int KPW = 64 / TPK;
     static_assert(CHUNKS % TPK == 0, "row chunks must split evenly over a key's threads");
 
-    const int S = p.num_splits;
+    // rows before split_row0 run unsplit (one workgroup each, first in the grid); the
+    // rest run num_splits ways
+    const int64_t R0 = p.split_row0;
+    const bool whole = (int64_t)blockIdx.x < R0;
+    const int S = whole ? 1 : p.num_splits;
+    const int64_t t_split = whole ? 0 : (int64_t)blockIdx.x - R0;
+    const int s = (int)(t_split % S);
+    const int64_t r = whole ? (int64_t)blockIdx.x : R0 + t_split / S;
     const int G = p.group;
-    const int s = (int)(blockIdx.x % S);
-    const int64_t r = blockIdx.x / S;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -93,8 +98,8 @@ gather_mfma_wide_kernel(GatherParams p)
     const bool head_real = head < G;
 
     const int64_t n = key_list_length(p, r);
-    const int64_t j0 = (int64_t)s * p.split_keys;
-    const int64_t j1 = n < j0 + p.split_keys ? n : j0 + p.split_keys;
+    const int64_t j0 = (int64_t)s * p.split_keys;                 // 0 for an unsplit row
+    const int64_t j1 = whole || n < j0 + p.split_keys ? n : j0 + p.split_keys;
     const int nb = j1 > j0 ? (int)((j1 - j0 + kWTile - 1) / kWTile) : 0;
     // steps: nb scores, then the value step of the last tile; a whole number of loop
     // trips so that register slots and LDS tiles stay static (extra steps idle)
@@ -114,7 +119,7 @@ gather_mfma_wide_kernel(GatherParams p)
             for (int t = 0; t < NDT; ++t)
                 store_out4(p.out, p.out_dtype, rh * D + 16 * t + 4 * lq, acc[t] * inv);
         } else {
-            const int64_t srh = (int64_t)s * p.total_q * p.num_q_heads + rh;
+            const int64_t srh = ((int64_t)s * (p.total_q - R0) + (r - R0)) * p.num_q_heads + gh;
 #pragma unroll
             for (int t = 0; t < NDT; ++t)
                 *reinterpret_cast<f32x4_t *>(p.ws_acc + srh * D + 16 * t + 4 * lq) = acc[t];
@@ -380,7 +385,7 @@ gather_mfma_wide_kernel(GatherParams p)
 template <int D>
 int launch_wide(const GatherParams &p, void *stream)
 {
-    const int64_t grid = p.total_q * (int64_t)p.num_splits;
+    const int64_t grid = p.split_row0 + (p.total_q - p.split_row0) * (int64_t)p.num_splits;
     if (grid <= 0)
         return 0;
     if (grid > 0x7fffffff)

@@ -19,6 +19,11 @@ constexpr int64_t kTargetWorkgroups = 256 * 2;
 // gathering.
 constexpr int64_t kMinKeysPerSplit = 128;
 constexpr int32_t kMaxSplits = 64;
+// Head-split matrix-core kernel: workgroups resident at once (one per CU), and the most
+// splits a tail row of a short last round is cut into (more would cost the combine
+// step more than the round saves).
+constexpr int64_t kWideSlots = 256;
+constexpr int64_t kMaxTailSplits = 8;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace
@@ -132,6 +137,7 @@ qsa_status plan_gather(const qsa_ragged_q *q, int64_t num_kv_heads, int32_t dtyp
         return fail(QSA_ERR_UNSUPPORTED,
                     "no kernel built for dtype %d, group %lld, head_dim %lld", dtype,
                     (long long)group, (long long)q->head_dim);
+    plan->split_row0 = 0;
     qsa_launch_options o = {0, 0, 0, 0};
     if (opts)
         o = *opts;
@@ -238,12 +244,31 @@ qsa_status plan_gather(const qsa_ragged_q *q, int64_t num_kv_heads, int32_t dtyp
     splits = ceil_div(cap, sk);   // drop splits that would start past the capacity
     if (splits < 1)
         splits = 1;
+    // head-split matrix-core kernel (one workgroup per CU): when the rows fill whole
+    // rounds of the 256 CUs plus a short last round, that round would run a few rows
+    // alone for a full row's time. Those tail rows run split instead (their partials
+    // merged by the combine step), the rows before them unsplit.
+    int64_t row0 = 0;
+    if (plan->path == PATH_MFMA_WIDE && o.num_splits == 0 && splits == 1) {
+        const int64_t tail = q->total_q % kWideSlots;
+        if (q->total_q > kWideSlots && tail > 0 && tail <= kWideSlots / 4) {
+            int64_t ts = kWideSlots / tail < kMaxTailSplits ? kWideSlots / tail : kMaxTailSplits;
+            const int64_t tsk = ceil_div(ceil_div(cap, ts), unit) * unit;
+            ts = ceil_div(cap, tsk);
+            if (ts > 1) {
+                row0 = q->total_q - tail;
+                splits = ts;
+                sk = tsk;
+            }
+        }
+    }
+    plan->split_row0 = row0;
     plan->num_splits = (int32_t)splits;
     plan->split_keys = sk;
     plan->ws_bytes = 0;
     plan->ws_ml_offset = 0;
     if (splits > 1) {
-        size_t rows_heads = (size_t)q->total_q * (size_t)q->num_q_heads;
+        size_t rows_heads = (size_t)(q->total_q - row0) * (size_t)q->num_q_heads;
         size_t acc = (size_t)splits * rows_heads * (size_t)q->head_dim * sizeof(float);
         acc = (acc + 255) & ~(size_t)255;
         plan->ws_ml_offset = acc;

@@ -76,13 +76,32 @@ def test_latent_large_sink_dominates():
 def test_c5_latent_full_size_sampled_rows():
     """The latent workload at full size (16 decode + 4 x 128 prefill rows, 64 heads,
     head_dim 512) in the default launch configuration; the oracle checks every
-    decode row and 8 rows of each prefill sequence."""
+    decode row, 8 rows of each prefill sequence and the last 16 rows (528 rows fill
+    two rounds of 256 CUs plus 16: those 16 run split, the others unsplit)."""
     announce("c5 full size: generating")
     case = W.c5_latent_bf16()
     off = case.input_row_offsets.astype(np.int64)
     rows = list(range(16))
     for b in range(16, case.batch):
         rows += [int(off[b]), int(off[b]) + 1] + [int(x) for x in np.linspace(off[b] + 2, off[b + 1] - 1, 6)]
+    rows = sorted(set(rows) | set(range(case.total_q - 16, case.total_q)))
     announce("c5 full size: running (%d rows checked)" % len(rows))
     got, ref = run(case, rows=rows)
     compare(got, ref, "bf16", "c5 full", rel_rms_max=0.01)
+
+
+@pytest.mark.parametrize("n_decode,tail", [(258, 2), (300, 44), (256 + 64, 64), (256 + 65, 65)])
+def test_latent_tail_rows_run_split(n_decode, tail):
+    """More rows than 256 CUs with a short last round: the last total_q mod 256 rows
+    (at most 64 of them) run split and are merged by the combine step, the rows before
+    them unsplit; with a longer last round every row runs unsplit. Every row checked."""
+    rng = np.random.default_rng(n_decode)
+    pos = rng.integers(30, 400, size=n_decode)
+    case = W.make_latent(name="lat_tail", seed=n_decode, decode_positions=pos, prefill_positions=[],
+                         prefill_rows=0, num_heads=64, head_dim=128, dtype="bf16", out_dtype="bf16", window=24,
+                         swa_page_size=16, comp_page_size=16, num_comp=40, comp_ratio=4, unused_frac=0.2,
+                         scale=1 / np.sqrt(128))
+    assert case.total_q % 256 == tail
+    announce("latent tail rows: %d rows (tail %d)" % (case.total_q, tail))
+    got, ref = run(case)
+    compare(got, ref, "bf16", "latent tail %d" % tail)
