@@ -1,6 +1,7 @@
 """fp64 CPU oracle for index-selected sparse attention over a paged KV cache (and for
-dense ragged attention without a cache, the comparison row, and for the key
-compression that produces the block keys).
+dense ragged attention without a cache, the comparison row, for the key
+compression that produces the block keys, and for the top-k block selection that
+turns them into token indices).
 
 TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package. The product library
@@ -15,7 +16,8 @@ Every function is pinned by ``tests/test_oracle_pins.py``; none is "parity
 unpinned" except where that file says so (the GQA head-to-kv-head mapping and the
 latent key-equals-value reading are conventions that no page value fixes; so are the
 key-compression choices of pooling operator, step order, rotation pairing and
-rotation position, which the pins check as stated but the pages do not fix).
+rotation position, and the whole contract of block selection, which the pins check
+as stated but the pages do not fix).
 """
 from __future__ import annotations
 
@@ -74,8 +76,9 @@ def load(path: str = None):
         lib.orc_dense.argtypes = [P, P, I64, P, P, P, I, I64, I64, I64, I64, P, I64, I, I64, F, I]
         lib.orc_compress.argtypes = [P, P, I, I64, I64, I64, I64, I64, I64, P, I64, I64, P, I64, I64, I64,
                                      P, P, I, I64, I64, F, I]
+        lib.orc_select.argtypes = [P, P, P, P, P, I, I64, I64, P, P, I64, I64, I64, I64, I64, I]
         for f in (lib.orc_decode, lib.orc_qsa, lib.orc_block_sparse, lib.orc_latent, lib.orc_dense,
-                  lib.orc_compress):
+                  lib.orc_compress, lib.orc_select):
             f.restype = I
         _libs[path] = lib
     return _libs[path]
@@ -243,6 +246,26 @@ def compress_keys(*, kv_blocks, dtype, num_pages, num_planes, num_layers, page_s
     return out
 
 
+def select_blocks(*, q_index, block_keys, dtype, input_row_offsets, cache_lengths, max_blocks, ratio, topk, W,
+                  with_blocks=True, fill=-7, nthreads=None, lib=None):
+    """Top-k block selection from block keys; returns (token_indices [total_q, W] int32 with
+    ``fill`` past each row's count, counts [total_q] int32, blocks [total_q, topk] int32
+    or None)."""
+    lib = lib or load()
+    keep = _Keep()
+    total_q, D = q_index.shape
+    off = np.asarray(input_row_offsets, np.uint32)
+    idx = np.full((total_q, W), fill, np.int32)
+    counts = np.zeros(total_q, np.int32)
+    blocks = np.full((total_q, topk), -9, np.int32) if with_blocks else None
+    rc = lib.orc_select(idx.ctypes.data, counts.ctypes.data, blocks.ctypes.data if with_blocks else None,
+                        keep.ptr(q_index), keep.ptr(block_keys), DT[dtype], total_q, D, keep.ptr(off),
+                        keep.ptr(np.asarray(cache_lengths, np.uint32)), len(off) - 1, max_blocks, ratio, topk, W,
+                        nthreads or default_threads())
+    _check(rc, "orc_select")
+    return idx, counts, blocks
+
+
 def _leaf(c):
     return dict(blocks=c.storage, num_pages=c.num_pages, num_layers=c.num_layers,
                 page_size=c.page_size, num_kv_heads=c.num_kv_heads, page_stride=c.page_stride,
@@ -285,6 +308,11 @@ def run_case(case, rows=None, nthreads=None, lib=None) -> np.ndarray:
                              layer_idx=case.layer_idx, key_counts=case.key_counts, max_blocks=case.max_blocks,
                              ratio=case.ratio, gamma=case.gamma, freqs_cis=case.freqs, freq_dtype=case.freq_dtype,
                              rotary_dim=case.rotary_dim, eps=case.eps, nthreads=nthreads, lib=lib)
+    if case.kind == "select":
+        return select_blocks(q_index=case.q_index, block_keys=case.block_keys, dtype=case.dtype,
+                             input_row_offsets=case.input_row_offsets, cache_lengths=case.cache_lengths,
+                             max_blocks=case.max_blocks, ratio=case.ratio, topk=case.topk, W=case.W,
+                             nthreads=nthreads, lib=lib)
     if case.kind == "dense":
         return dense_attention(q=case.q, k=case.k, v=case.v, dtype=case.dtype,
                                input_row_offsets=case.input_row_offsets, causal=case.causal,

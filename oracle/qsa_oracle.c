@@ -31,7 +31,8 @@
  *   - "QSACompressKeysPaged": summary, Tensor shapes, execute Parameters and Args
  *     (block_keys [batch * max_blocks, head_dim], gamma [head_dim], freqs_cis
  *     [positions, rotary_dim] of cos/sin pairs, key_counts = raw keys per sequence
- *     this step included, ratio, rotary_dim, eps).
+ *     this step included, ratio, rotary_dim, eps; the per-sequence stride max_blocks
+ *     that the block scorer re-derives, which names the selection step).
  *
  * Readings where the pages are silent (listed in the design notes of the repo):
  *   - query head h reads kv head h / group (consecutive groups);
@@ -49,7 +50,12 @@
  *     trailing partial group gives no block key); the order is pool, then RMS-norm
  *     with gamma, then rotation; the rotation turns interleaved channel pairs
  *     (2i, 2i+1) below rotary_dim by the table's (cos, sin) pair at the block's first
- *     raw position j * ratio; raw keys sit in plane 0 (K) of the indexer cache.
+ *     raw position j * ratio; raw keys sit in plane 0 (K) of the indexer cache;
+ *   - block selection (no page gives its contract; parity unpinned for these choices):
+ *     one index query vector per row, the score of a block is its dot product with the
+ *     block key, the top-k complete blocks are kept (equal scores: lower index first),
+ *     the row always keeps its incomplete group, and positions are emitted in
+ *     increasing order.
  *
  * Parity pins: every function here is pinned by tests/test_oracle_pins.py
  * (closed forms, invariants, brute-force dense masked attention, exhaustive
@@ -571,6 +577,98 @@ int orc_compress(double *out, const void *blocks, int dt, int64_t num_pages, int
             }
         free(row);
         free(x);
+    }
+    return err;
+}
+
+/* ------------------------------------------------------- selection producer */
+
+typedef struct {
+    double s;
+    int64_t j;
+} orc_scored;
+
+/* Higher score first; equal scores: lower block index first. */
+static int cmp_scored(const void *a, const void *b)
+{
+    const orc_scored *x = a, *y = b;
+    if (x->s != y->s)
+        return x->s > y->s ? -1 : 1;
+    return x->j < y->j ? -1 : x->j > y->j;
+}
+
+static int cmp_i64(const void *a, const void *b)
+{
+    int64_t x = *(const int64_t *)a, y = *(const int64_t *)b;
+    return x < y ? -1 : x > y;
+}
+
+/* Block selection from block keys (the step "QSACompressKeysPaged" names as the
+ * consumer of its block keys, qsa_block_score, followed by a top-k). Row r of sequence b
+ * at position pos = cache_lengths[b] + (r - row_off[b]) has (pos + 1) / ratio complete
+ * blocks and sees those with j < nv = min((pos + 1) / ratio, max_blocks); block j scores
+ * s_j = sum_d q_index[r, d] * block_keys[b * max_blocks + j, d]. The k = min(topk, nv)
+ * highest scores are kept (equal scores: the lower block index first). Output, per row:
+ * token_indices[r, :] = the positions j*ratio .. j*ratio + ratio - 1 of the kept blocks
+ * in increasing j, then the positions of the row's incomplete group,
+ * ((pos + 1) / ratio) * ratio .. pos (fewer than ratio); counts[r] = k*ratio + that
+ * group's size; blocks[r, 0:k] = the kept j in increasing
+ * order and -1 after (when blocks is not NULL). Entries of token_indices at or past
+ * counts[r] are left as they were. */
+int orc_select(int32_t *token_indices, int32_t *counts, int32_t *blocks, const void *q_index,
+               const void *block_keys, int dt, int64_t total_q, int64_t D, const uint32_t *row_off,
+               const uint32_t *cache_lengths, int64_t batch, int64_t max_blocks, int64_t ratio, int64_t topk,
+               int64_t W, int nthreads)
+{
+    if (ratio < 1 || topk < 0 || max_blocks < 0 || W < topk * ratio + ratio - 1)
+        return ORC_EINPUT;
+    int err = ORC_OK;
+#pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1)
+    {
+        orc_scored *sc = malloc(sizeof(orc_scored) * (max_blocks > 0 ? max_blocks : 1));
+        int64_t *kept = malloc(sizeof(int64_t) * (topk > 0 ? topk : 1));
+        if (!sc || !kept) {
+#pragma omp atomic write
+            err = ORC_ENOMEM;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < total_q; ++r) {
+            if (err)
+                continue;
+            int64_t b = seq_of_row(row_off, batch, r);
+            if (b < 0) {
+#pragma omp atomic write
+                err = ORC_EINPUT;
+                continue;
+            }
+            int64_t pos = (int64_t)cache_lengths[b] + (r - (int64_t)row_off[b]);
+            int64_t nfull = (pos + 1) / ratio;
+            int64_t nv = nfull < max_blocks ? nfull : max_blocks;
+            for (int64_t j = 0; j < nv; ++j) {
+                double s = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    s += elem(q_index, dt, r * D + d) * elem(block_keys, dt, (b * max_blocks + j) * D + d);
+                sc[j].s = s;
+                sc[j].j = j;
+            }
+            int64_t k = topk < nv ? topk : nv;
+            qsort(sc, (size_t)nv, sizeof(orc_scored), cmp_scored);
+            for (int64_t m = 0; m < k; ++m)
+                kept[m] = sc[m].j;
+            qsort(kept, (size_t)k, sizeof(int64_t), cmp_i64);
+            int64_t n = 0;
+            for (int64_t m = 0; m < k; ++m)
+                for (int64_t t = 0; t < ratio; ++t)
+                    token_indices[r * W + n++] = (int32_t)(kept[m] * ratio + t);
+            for (int64_t p = nfull * ratio; p <= pos; ++p)
+                token_indices[r * W + n++] = (int32_t)p;
+            counts[r] = (int32_t)n;
+            if (blocks)
+                for (int64_t m = 0; m < topk; ++m)
+                    blocks[r * topk + m] = m < k ? (int32_t)kept[m] : -1;
+        }
+        free(sc);
+        free(kept);
     }
     return err;
 }

@@ -771,4 +771,82 @@ def pin_compress_scale_invariance_without_eps(lib):
     assert_same_rows(oracle.run_case(c2, lib=lib), base, 1e-12, "compress scale invariance")
 
 
+# ------------------------------------------------------------------ pins: block selection
+
+def small_select_cases():
+    return [
+        W.make_select(name="sel_int", seed=51, rows=[1, 3, 2, 1], cache_lengths=[40, 23, 2, 77], head_dim=16,
+                      dtype="bf16", ratio=4, topk=5, integer=True),
+        W.make_select(name="sel_f32", seed=52, rows=[2, 1, 4], cache_lengths=[100, 9, 60], head_dim=32,
+                      dtype="f32", ratio=3, topk=7),
+        W.make_select(name="sel_cap", seed=53, rows=[1, 2], cache_lengths=[90, 200], head_dim=8, dtype="bf16",
+                      ratio=4, topk=6, max_blocks=20, integer=True),
+        W.make_select(name="sel_r1", seed=54, rows=[3, 1], cache_lengths=[12, 0], head_dim=16, dtype="bf16",
+                      ratio=1, topk=4, W=9),
+    ]
+
+
+def numpy_select(case):
+    """Selection from library routines: fp64 scores by numpy matrix products and the
+    order (score descending, block index ascending) by numpy.lexsort."""
+    q = case.q_index.to(torch.float32).to(torch.float64).numpy()
+    bk = case.block_keys.to(torch.float32).to(torch.float64).numpy().reshape(case.batch, case.max_blocks, -1)
+    off = case.input_row_offsets.astype(np.int64)
+    pos = case.positions()
+    rows = []
+    for r in range(case.total_q):
+        b = int(np.searchsorted(off, r, side="right") - 1)
+        nfull = (pos[r] + 1) // case.ratio
+        nv = min(nfull, case.max_blocks)
+        s = bk[b, :nv] @ q[r]
+        order = np.lexsort((np.arange(nv), -s))
+        kept = np.sort(order[:min(case.topk, nv)])
+        toks = [int(j) * case.ratio + t for j in kept for t in range(case.ratio)]
+        toks += list(range(nfull * case.ratio, pos[r] + 1))
+        rows.append((toks, kept))
+    return rows
+
+
+def check_select(case, got, what):
+    idx, counts, blocks = got
+    for r, (toks, kept) in enumerate(numpy_select(case)):
+        assert counts[r] == len(toks), "%s row %d: count %d != %d" % (what, r, counts[r], len(toks))
+        assert idx[r, :counts[r]].tolist() == toks, "%s row %d: token indices differ" % (what, r)
+        assert (idx[r, counts[r]:] == -7).all(), "%s row %d: wrote past the count" % (what, r)
+        exp = list(kept) + [-1] * (case.topk - len(kept))
+        assert blocks[r].tolist() == exp, "%s row %d: blocks %s != %s" % (what, r, blocks[r].tolist(), exp)
+
+
+def pin_select_matches_numpy_lexsort(lib):
+    for case in small_select_cases():
+        check_select(case, oracle.run_case(case, lib=lib), case.name)
+
+
+def pin_select_closed_forms(lib):
+    """A zero query scores every block 0: the first k blocks win (ties go to the lower
+    index). A row before its first complete group keeps only its own positions. A
+    planted block (the query itself, scaled up) always wins."""
+    case = W.make_select(name="sel_zero", seed=55, rows=[1, 1, 1], cache_lengths=[50, 2, 30], head_dim=16,
+                         dtype="f32", ratio=4, topk=3)
+    case.q_index = torch.zeros_like(case.q_index)
+    idx, counts, blocks = oracle.run_case(case, lib=lib)
+    assert blocks[0].tolist() == [0, 1, 2] and counts[0] == 12 + 3           # pos 50: 12 complete, 3 tail
+    assert idx[0, :15].tolist() == list(range(12)) + [48, 49, 50]
+    assert counts[1] == 3 and idx[1, :3].tolist() == [0, 1, 2] and blocks[1].tolist() == [-1, -1, -1]
+    case = W.make_select(name="sel_plant", seed=56, rows=[1], cache_lengths=[200], head_dim=16, dtype="f32",
+                         ratio=4, topk=1)
+    case.block_keys = case.block_keys.clone()
+    case.block_keys[37] = case.q_index[0] * 8
+    idx, counts, blocks = oracle.run_case(case, lib=lib)
+    assert blocks[0].tolist() == [37] and idx[0, :4].tolist() == [148, 149, 150, 151]
+
+
+def pin_select_positive_scale_invariance(lib):
+    for case in small_select_cases()[:2]:
+        base = oracle.run_case(case, lib=lib)
+        c2 = W.SelectCase(**{**case.__dict__, "q_index": case.q_index * 4})
+        got = oracle.run_case(c2, lib=lib)
+        assert all(np.array_equal(a, b) for a, b in zip(base, got)), "scaling the query changed the selection"
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

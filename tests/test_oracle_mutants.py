@@ -57,6 +57,12 @@ MUTANTS = [
     ("compress_rotation_past_rotary_dim", "2 * i + 1 < rotary_dim; ++i)", "2 * i + 1 < D; ++i)"),
     ("compress_cos_sin_swapped", "double cs = elem(freqs, fdt, p * rotary_dim + 2 * i);",
      "double cs = elem(freqs, fdt, p * rotary_dim + 2 * i + 1);"),
+    ("select_ties_reversed", "return x->j < y->j ? -1 : x->j > y->j;", "return x->j > y->j ? -1 : x->j < y->j;"),
+    ("select_candidates_off_by_one", "int64_t nfull = (pos + 1) / ratio;", "int64_t nfull = pos / ratio;"),
+    ("select_tail_short", "for (int64_t p = nfull * ratio; p <= pos; ++p)", "for (int64_t p = nfull * ratio; p < pos; ++p)"),
+    ("select_not_ascending", "qsort(kept, (size_t)k, sizeof(int64_t), cmp_i64);", "(void)cmp_i64;"),
+    ("select_lowest_scores", "sc[j].s = s;", "sc[j].s = -s;"),
+    ("select_wrong_sequence", "elem(block_keys, dt, (b * max_blocks + j) * D + d)", "elem(block_keys, dt, j * D + d)"),
     ("compress_last_block_dropped", "for (int64_t j = 0; j < max_blocks; ++j) {",
      "for (int64_t j = 0; j < max_blocks - 1; ++j) {"),
 ]

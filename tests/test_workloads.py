@@ -69,3 +69,14 @@ def test_compress_recipe():
                                                        torch.ones(12, 2, dtype=torch.float64), atol=1e-6)
     # 2 blocks x 4 keys x 16 B + 2 written x 16 B + 2 table rows x 16 B + gamma 16 B + 2 counts + 2 lut entries
     assert W.compress_bytes(c) == 128 + 32 + 32 + 16 + 8 + 8
+
+
+def test_select_recipe():
+    c = W.make_select(seed=6, rows=[2, 1], cache_lengths=[9, 0], head_dim=8, dtype="bf16", ratio=4, topk=2,
+                      integer=True)
+    assert c.max_blocks == 2 and c.W == 11
+    assert c.positions().tolist() == [9, 10, 0] and c.candidates().tolist() == [2, 2, 0]
+    bk = c.block_keys.view(2, 2, 8)
+    assert not bk[0].isnan().any() and bk[1].isnan().all()          # sequence 1 has no complete block
+    v = c.q_index.float()
+    assert (v == v.round()).all() and v.abs().max() <= 2

@@ -478,6 +478,79 @@ def make_compress(*, name="compress", seed, cache_lengths, rows, page_size, num_
                         max(rows) if rows else 0)
 
 
+# --------------------------------------------------------------------------- block selection
+
+@dataclass
+class SelectCase:
+    """One block-selection call: an index query per row, block keys [batch * max_blocks, D]
+    at a per-sequence stride, top-k complete blocks into token_indices [total_q, W]."""
+    name: str
+    seed: int
+    dtype: str
+    q_index: torch.Tensor          # [total_q, D]
+    block_keys: torch.Tensor       # [batch * max_blocks, D]
+    input_row_offsets: np.ndarray  # [batch + 1] uint32
+    cache_lengths: np.ndarray      # [batch] uint32
+    max_blocks: int
+    ratio: int
+    topk: int
+    W: int
+    max_prompt_length: int
+    kind: str = "select"
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def total_q(self) -> int:
+        return self.q_index.shape[0]
+
+    @property
+    def batch(self) -> int:
+        return len(self.input_row_offsets) - 1
+
+    def positions(self) -> np.ndarray:
+        off = self.input_row_offsets.astype(np.int64)
+        pos = np.empty(self.total_q, np.int64)
+        for b in range(self.batch):
+            pos[off[b]:off[b + 1]] = int(self.cache_lengths[b]) + np.arange(off[b + 1] - off[b])
+        return pos
+
+    def candidates(self) -> np.ndarray:
+        """Complete blocks each row may choose from."""
+        return np.minimum((self.positions() + 1) // self.ratio, self.max_blocks)
+
+
+def make_select(*, name="select", seed, rows, cache_lengths, head_dim, dtype, ratio, topk, W=None,
+                max_blocks=None, integer=False) -> SelectCase:
+    """Block-selection inputs: index queries and block keys N(0, 1) in ``dtype`` (or, with
+    ``integer``, whole numbers in [-2, 2], whose dot products are exact in fp32, so equal
+    scores are frequent and the tie rule is exercised). Block rows past a sequence's
+    complete blocks are NaN. W defaults to topk * ratio + ratio - 1."""
+    rng = np.random.default_rng(seed)
+    rows = [int(x) for x in rows]
+    cl = np.asarray([int(x) for x in cache_lengths], np.uint32)
+    off = _row_offsets(rows)
+    total_q = int(off[-1])
+    keys_per_seq = [int(c) + r for c, r in zip(cl, rows)]
+    if max_blocks is None:
+        max_blocks = max(1, max(k // ratio for k in keys_per_seq)) if rows else 1
+    batch = len(rows)
+    if integer:
+        q = torch.from_numpy(rng.integers(-2, 3, size=(total_q, head_dim)).astype(np.float32))
+        bk = torch.from_numpy(rng.integers(-2, 3, size=(batch * max_blocks, head_dim)).astype(np.float32))
+        q, bk = q.to(TORCH_DTYPE[dtype]), bk.to(TORCH_DTYPE[dtype])
+    else:
+        q = _normal((total_q, head_dim), seed, 4, 1.0, dtype)
+        bk = _normal((batch * max_blocks, head_dim), seed, 5, 1.0, dtype)
+    bkv = bk.view(batch, max_blocks, head_dim)
+    for b in range(batch):
+        nb = min(keys_per_seq[b] // ratio, max_blocks)
+        nan_fill_(bkv[b, nb:])
+    if W is None:
+        W = topk * ratio + ratio - 1
+    return SelectCase(name, seed, dtype, q, bk, off, cl, int(max_blocks), int(ratio), int(topk), int(W),
+                      max(rows) if rows else 0, meta={"integer": integer})
+
+
 # --------------------------------------------------------------------------- named workloads
 
 def c1_tiny_fp32(seed=1):
