@@ -17,8 +17,9 @@ fraction of the 8 TB/s HBM peak, a roofline object for the gather kernel timed w
 HIP events around that kernel alone, the fp64 CPU oracle timed on the host as a
 baseline, and the same step measurements for the other workloads (ragged prefill
 with 16 q heads per kv head, block-sparse e4m3 top-16 decode and speculative decode,
-latent window + compressed + sink, dense causal prefill without a cache, and the key
-compression that produces the block keys) under "other_workloads".
+latent window + compressed + sink, dense causal prefill without a cache, the key
+compression that produces the block keys, and the top-k block selection that turns
+them into token indices) under "other_workloads".
 """
 from __future__ import annotations
 
@@ -291,6 +292,43 @@ def compress_workload(name, make, R, dev, stream, steps, warmup):
     return res
 
 
+def select_workload(name, make, dev, stream, steps, warmup):
+    """Top-k block selection (scores of every visible block key, then a radix top-k per
+    row): block keys and queries read once per row; token indices, counts and block ids
+    written."""
+    import numpy as np
+    import torch
+    import oracle
+    import workloads as W
+    from workloads import device as D
+    log("%s: generating" % name)
+    case = make()
+    dc = D.select_to_device(case, dev)
+    idx = torch.empty((case.total_q, case.W), dtype=torch.int32, device=dev)
+    counts = torch.empty(case.total_q, dtype=torch.int32, device=dev)
+    blocks = torch.empty((case.total_q, case.topk), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    log("%s: timing %d steps (+ %d with kernel events)" % (name, steps, steps))
+    ms_step, kern = time_step_fn(lambda k: D.run_select(dc, token_indices=idx, counts=counts, blocks=blocks,
+                                                        stream=stream), steps, warmup)
+    nv = case.candidates()
+    eb = W.ELEM_BYTES[case.dtype]
+    D_ = case.q_index.shape[1]
+    cnt = counts.cpu().numpy()
+    algo = int(nv.sum()) * D_ * eb + case.total_q * D_ * eb + int(cnt.sum()) * 4 + case.total_q * (4 + 4 * case.topk)
+    ref = oracle.run_case(case)
+    res = {"workload": name, "rows": case.total_q, "candidate_blocks": int(nv.sum()), "topk": case.topk,
+           "dtype": case.dtype, "algorithmic_bytes_per_step": algo, "steps": steps,
+           "ms_per_step": round(ms_step, 5), "select_kernels_avg_us": round(kern * 1e3, 2),
+           "select_GBps": round(algo / (kern * 1e-3) / 1e9, 1),
+           "rows_per_s": round(case.total_q / (ms_step * 1e-3), 1),
+           "unit_of_work": "(row, candidate block): D*elem block-key bytes (+ the query, indices, counts, ids)",
+           "counts_match_oracle": bool(np.array_equal(cnt, ref[1]))}
+    del dc, idx, counts, blocks
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(case, budget_s):
     """The fp64 oracle on the host cores over the whole workload, repeated for about
     `budget_s` seconds (at least once)."""
@@ -326,6 +364,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="run one of the other workloads alone (for profiling) and print its JSON object")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after warmup, run one device-to-device copy of this many MiB (a kernel "
                          "of known traffic for calibrating hardware byte counters)")
@@ -346,13 +386,6 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
-    log("generating c2_decode_bf16 (seed 2)")
-    case = W.c2_decode_bf16()
-    a = algorithmic(case)
-    gathered = a["gathered"]
-    log("to device (%.2f GB pool x %d copies)" % (case.kv.storage.numel() * 2 / 1e9, args.replicas))
-    opts = {"num_splits": args.splits, "waves": args.waves, "unroll": args.unroll}
-    calls, ws, out = prepare(case, args.replicas, dev, opts)
     if args.copy_probe_mib:
         src = torch.ones(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -360,6 +393,34 @@ def main():
         torch.cuda.synchronize()
         log("copy probe: %d bytes read, %d bytes written" % (src.numel(), dst.numel()))
         del src, dst
+    n_other = max(5, min(args.steps, 20))
+    others = {
+        "c3_prefill_bf16": lambda: other_workload("c3_prefill_bf16", W.c3_prefill_bf16, 1, dev, stream, n_other, 3),
+        "c4_block_sparse_fp8": lambda: other_workload("c4_block_sparse_fp8", W.c4_block_sparse_fp8, 8, dev, stream,
+                                                      n_other, 3),
+        "c4s_block_sparse_spec_fp8": lambda: other_workload("c4s_block_sparse_spec_fp8", W.c4s_block_sparse_spec_fp8,
+                                                            8, dev, stream, n_other, 3),
+        "c5_latent_bf16": lambda: other_workload("c5_latent_bf16", W.c5_latent_bf16, 4, dev, stream, n_other, 3),
+        "f3_dense_prefill_bf16": lambda: other_workload("f3_dense_prefill_bf16", W.f3_dense_prefill_bf16, 1, dev,
+                                                        stream, n_other, 3),
+        "f2_compress_keys_bf16": lambda: compress_workload("f2_compress_keys_bf16", W.f2_compress_keys_bf16, 4, dev,
+                                                          stream, n_other, 3),
+        "f4_select_blocks_bf16": lambda: select_workload("f4_select_blocks_bf16", W.f4_select_blocks_bf16, dev,
+                                                        stream, n_other, 3),
+    }
+    if args.only:
+        if args.only not in others:
+            print("unknown workload %s (one of %s)" % (args.only, ", ".join(others)), file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps(others[args.only]()), flush=True)
+        return
+    log("generating c2_decode_bf16 (seed 2)")
+    case = W.c2_decode_bf16()
+    a = algorithmic(case)
+    gathered = a["gathered"]
+    log("to device (%.2f GB pool x %d copies)" % (case.kv.storage.numel() * 2 / 1e9, args.replicas))
+    opts = {"num_splits": args.splits, "waves": args.waves, "unroll": args.unroll}
+    calls, ws, out = prepare(case, args.replicas, dev, opts)
     log("timing %d steps (+ %d with kernel events)" % (args.steps, args.steps))
     ms_step, kern_avg = time_steps(calls, opts, out, ws, stream, args.steps, args.warmup)
 
@@ -408,15 +469,7 @@ def main():
     del calls, ws, out
     torch.cuda.empty_cache()
     if not args.no_other_workloads:
-        n = max(5, min(args.steps, 20))
-        res["other_workloads"] = [
-            other_workload("c3_prefill_bf16", W.c3_prefill_bf16, 1, dev, stream, n, 3),
-            other_workload("c4_block_sparse_fp8", W.c4_block_sparse_fp8, 8, dev, stream, n, 3),
-            other_workload("c4s_block_sparse_spec_fp8", W.c4s_block_sparse_spec_fp8, 8, dev, stream, n, 3),
-            other_workload("c5_latent_bf16", W.c5_latent_bf16, 4, dev, stream, n, 3),
-            other_workload("f3_dense_prefill_bf16", W.f3_dense_prefill_bf16, 1, dev, stream, n, 3),
-            compress_workload("f2_compress_keys_bf16", W.f2_compress_keys_bf16, 4, dev, stream, n, 3),
-        ]
+        res["other_workloads"] = [run_other() for run_other in others.values()]
     if not args.no_cpu_baseline:
         log("cpu baseline (~%.0f s)" % args.cpu_seconds)
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)

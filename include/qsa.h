@@ -16,8 +16,9 @@
  *                                ("latent_sparse_attention_ragged_paged", summary,
  *                                Parameters and Args).
  *
- * and the key compression that produces the block keys block selection scores
- * (qsa_compress_keys, "QSACompressKeysPaged").
+ * and the steps that produce a selection: the key compression that pools raw index
+ * keys into block keys (qsa_compress_keys, "QSACompressKeysPaged") and the top-k block
+ * selection that turns them into token_indices and counts (qsa_select_blocks).
  *
  * Conventions shared by every entry point:
  *   - Pointers are DEVICE pointers unless a comment says (host). The caller owns
@@ -55,7 +56,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 3
+#define QSA_ABI_VERSION 4
 
 /* Element types. QSA_FP8_E4M3 is the OCP 8-bit E4M3 "fn" format (bias 7, max 448,
  * no infinity), scale-free as the block-sparse page states for its FP8 path. */
@@ -277,6 +278,45 @@ qsa_status qsa_compress_keys(void *block_keys, int64_t max_blocks, const void *g
                              const int32_t *key_counts, const qsa_paged_cache *kv, int64_t batch,
                              uint32_t layer_idx, uint32_t max_prompt_length, int64_t ratio, float eps,
                              void *stream);
+
+/* ------------------------------------------------------------------------- */
+/* Block selection: the step between key compression and sparse attention. The
+ * "QSACompressKeysPaged" page names its consumer (a block scorer that re-derives the
+ * per-sequence stride max_blocks) but gives it no contract; the rule here is this
+ * library's reading.
+ *
+ * Row r of sequence b, at position pos = cache_lengths[b] + (r - input_row_offsets[b]),
+ * has nfull = (pos + 1) / ratio complete blocks and chooses among j < nv =
+ * min(nfull, max_blocks). Block j scores q_index[r, :] . block_keys[b * max_blocks + j, :]
+ * (fp32 sum of products). The k = min(topk, nv) highest scores are kept; equal scores go
+ * to the lower block index. Output:
+ *   token_indices[r, :]  the positions j*ratio .. j*ratio + ratio - 1 of the kept blocks in
+ *                        increasing j, then the row's incomplete group nfull*ratio .. pos;
+ *                        entries at or past counts[r] are not written
+ *   counts[r]            k * ratio + (pos + 1 - nfull * ratio)
+ *   blocks[r, 0:topk]    (optional, may be NULL) the kept j in increasing order, then -1
+ * token_indices and counts are in the format qsa_sparse_attention reads.
+ *
+ *   q_index       ragged rows with num_q_heads == 1 (one index query per row), dtype F32 or
+ *                 BF16, head_dim * element size a power of two in [16, 1024] bytes
+ *   block_keys    [batch * max_blocks, head_dim] of q_index->dtype, 16-byte aligned (e.g.
+ *                 qsa_compress_keys' block_keys); rows past a sequence's complete blocks
+ *                 are never read
+ *   cache_lengths [batch] (device); max_cache_length and q_index->max_prompt_length (host)
+ *                 bound the candidates a launch covers when their sum is non-zero:
+ *                 min(max_blocks, that sum / ratio) must be at most 32768
+ *   selection_width >= topk * ratio + ratio - 1
+ *   workspace     qsa_select_blocks_workspace_size bytes (fp32 scores), 16-byte aligned
+ * Scores are fp32: blocks whose scores differ by less than fp32 rounding may be chosen
+ * either way. The timing hook brackets both kernels of a call.
+ */
+qsa_status qsa_select_blocks_workspace_size(const qsa_ragged_q *q_index, int64_t max_blocks, int64_t ratio,
+                                            int64_t topk, uint32_t max_cache_length, size_t *bytes);
+
+qsa_status qsa_select_blocks(int32_t *token_indices, int64_t selection_width, int32_t *counts, int32_t *blocks,
+                             const qsa_ragged_q *q_index, const void *block_keys, int64_t max_blocks,
+                             const uint32_t *cache_lengths, uint32_t max_cache_length, int64_t ratio, int64_t topk,
+                             void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------- */
 /* Text describing the last non-OK status returned on the calling thread. */

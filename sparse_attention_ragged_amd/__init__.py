@@ -15,7 +15,9 @@ Entry points (same names as the C ABI, without the ``qsa_`` prefix):
   entries + per-head sink ("latent_sparse_attention_ragged_paged");
 * ``ragged_attention`` - dense ragged attention without a cache ("RaggedFlashAttentionGPU");
 * ``compress_keys`` - block keys pooled from the raw index keys of a paged indexer
-  cache ("QSACompressKeysPaged").
+  cache ("QSACompressKeysPaged");
+* ``select_blocks`` - top-k blocks per row from the block keys, as token_indices and
+  counts for ``sparse_attention``.
 """
 from __future__ import annotations
 
@@ -41,6 +43,7 @@ EXPORTS = (
     "qsa_block_sparse_attention_workspace_size", "qsa_block_sparse_attention",
     "qsa_latent_sparse_attention_workspace_size", "qsa_latent_sparse_attention",
     "qsa_ragged_attention_workspace_size", "qsa_ragged_attention", "qsa_compress_keys",
+    "qsa_select_blocks_workspace_size", "qsa_select_blocks",
     "qsa_last_error", "qsa_abi_version", "qsa_struct_size", "qsa_set_timing_events",
 )
 
@@ -98,10 +101,13 @@ def _load():
     lib.qsa_ragged_attention.argtypes = [P, I32, pr, P, P, I64, I32, I64, F, po, P, SZ, P]
     U32 = ctypes.c_uint32
     lib.qsa_compress_keys.argtypes = [P, I64, P, P, I32, I64, I64, P, pc, I64, U32, U32, I64, F, P]
+    lib.qsa_select_blocks_workspace_size.argtypes = [pr, I64, I64, I64, U32, ctypes.POINTER(SZ)]
+    lib.qsa_select_blocks.argtypes = [P, I64, P, P, pr, P, I64, P, U32, I64, I64, P, SZ, P]
     for name in ("qsa_sparse_attention_workspace_size", "qsa_sparse_attention",
                  "qsa_block_sparse_attention_workspace_size", "qsa_block_sparse_attention",
                  "qsa_latent_sparse_attention_workspace_size", "qsa_latent_sparse_attention",
-                 "qsa_ragged_attention_workspace_size", "qsa_ragged_attention", "qsa_compress_keys"):
+                 "qsa_ragged_attention_workspace_size", "qsa_ragged_attention", "qsa_compress_keys",
+                 "qsa_select_blocks_workspace_size", "qsa_select_blocks"):
         getattr(lib, name).restype = ctypes.c_int
     lib.qsa_last_error.restype = ctypes.c_char_p
     lib.qsa_abi_version.restype = I32
@@ -386,6 +392,56 @@ def compress_keys(kv: PagedCache, key_counts, gamma, freqs_cis, layer_idx: int, 
                                  key_counts.data_ptr(), ctypes.byref(ck), batch, layer_idx, max_prompt_length,
                                  ratio, eps, _stream(kv.blocks, stream)))
     return out
+
+
+def select_blocks_workspace_size(q_index, input_row_offsets, max_blocks: int, ratio: int, topk: int,
+                                 max_cache_length: int = 0, max_prompt_length: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    rq = _ragged(q_index.unsqueeze(1) if q_index.dim() == 2 else q_index, input_row_offsets, max_prompt_length)
+    _check(lib.qsa_select_blocks_workspace_size(ctypes.byref(rq), max_blocks, ratio, topk, max_cache_length,
+                                                ctypes.byref(n)))
+    return n.value
+
+
+def select_blocks(q_index, input_row_offsets, block_keys, cache_lengths, max_blocks: int, ratio: int, topk: int, *,
+                  selection_width: int = 0, max_cache_length: int = 0, max_prompt_length: int = 0,
+                  with_blocks: bool = True, token_indices=None, counts=None, blocks=None, workspace=None,
+                  stream=None):
+    """Top-k blocks per row from the block keys. q_index [total_q, head_dim] (one index
+    query per row), block_keys [batch * max_blocks, head_dim] of the same dtype. Returns
+    (token_indices [total_q, W] int32, counts [total_q] int32, blocks [total_q, topk] int32
+    or None); W defaults to topk * ratio + ratio - 1. Entries of token_indices past a
+    row's count keep what the tensor held (uninitialised when it is allocated here)."""
+    q3 = q_index.unsqueeze(1) if q_index.dim() == 2 else q_index
+    _need_gpu(q3, block_keys, cache_lengths, token_indices, counts, blocks)
+    _need_i32(cache_lengths)
+    if block_keys.dtype != q3.dtype or block_keys.dim() != 2 or block_keys.shape[1] != q3.shape[2]:
+        raise ValueError("block_keys must be [batch * max_blocks, head_dim] of q_index's dtype")
+    W = selection_width or topk * ratio + ratio - 1
+    total_q, dev = q3.shape[0], q3.device
+    rq = _ragged(q3, input_row_offsets, max_prompt_length)
+    n = ctypes.c_size_t(0)
+    _check(lib.qsa_select_blocks_workspace_size(ctypes.byref(rq), max_blocks, ratio, topk, max_cache_length,
+                                                ctypes.byref(n)))
+    if workspace is None and n.value > 0:
+        workspace = torch.empty(n.value, dtype=torch.uint8, device=dev)
+    elif workspace is not None and workspace.numel() * workspace.element_size() < n.value:
+        raise ValueError("workspace too small: %d bytes needed" % n.value)
+    if token_indices is None:
+        token_indices = torch.empty((total_q, W), dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.empty(total_q, dtype=torch.int32, device=dev)
+    if blocks is None and with_blocks and topk > 0:
+        blocks = torch.empty((total_q, topk), dtype=torch.int32, device=dev)
+    if tuple(token_indices.shape) != (total_q, W) or counts.numel() != total_q:
+        raise ValueError("token_indices must be [total_q, %d] and counts [total_q]" % W)
+    _check(lib.qsa_select_blocks(token_indices.data_ptr(), W, counts.data_ptr(),
+                                 blocks.data_ptr() if blocks is not None else None, ctypes.byref(rq),
+                                 block_keys.data_ptr(), max_blocks, cache_lengths.data_ptr(), max_cache_length, ratio,
+                                 topk, workspace.data_ptr() if workspace is not None else None,
+                                 workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                 _stream(q3, stream)))
+    return token_indices, counts, blocks
 
 
 def set_timing_events(start, stop) -> None:

@@ -472,6 +472,108 @@ qsa_status qsa_compress_keys(void *block_keys, int64_t max_blocks, const void *g
     return QSA_OK;
 }
 
+// Candidate blocks per row a selection launch covers (0 when none).
+static int64_t select_bound(int64_t max_blocks, int64_t ratio, uint32_t max_cache_length, uint32_t max_prompt_length)
+{
+    int64_t bound = max_blocks;
+    const int64_t hint = (int64_t)max_cache_length + (int64_t)max_prompt_length;
+    if (hint > 0 && hint / ratio < bound)
+        bound = hint / ratio;
+    return bound;
+}
+
+static qsa_status select_check(const qsa_ragged_q *q, int64_t max_blocks, int64_t ratio, int64_t topk,
+                               uint32_t max_cache_length, int64_t *bound)
+{
+    if (!q)
+        return fail(QSA_ERR_NULL, "q_index descriptor is NULL");
+    if (!q->input_row_offsets)
+        return fail(QSA_ERR_NULL, "input_row_offsets is required");
+    if (q->total_q < 0 || q->batch < 1 || q->num_q_heads != 1 || q->head_dim < 1)
+        return fail(QSA_ERR_SHAPE, "q_index: total_q >= 0, batch >= 1, one head, head_dim >= 1");
+    if (q->total_q > (int64_t(1) << 31) - 1 || q->batch > (int64_t(1) << 31) - 1)
+        return fail(QSA_ERR_SHAPE, "q_index: total_q or batch out of range");
+    if (!select_supported(q->dtype, (int32_t)std::min<int64_t>(q->head_dim, 1 << 20)))
+        return fail(q->dtype == QSA_F32 || q->dtype == QSA_BF16 ? QSA_ERR_UNSUPPORTED : QSA_ERR_DTYPE,
+                    "block selection takes F32 or BF16 queries and keys whose rows are 16, 32, 64, ... or "
+                    "1024 bytes (dtype %d, head_dim %lld)", q->dtype, (long long)q->head_dim);
+    if (ratio < 1 || ratio > (int64_t(1) << 20) || topk < 0 || topk > (int64_t(1) << 24) || max_blocks < 0)
+        return fail(QSA_ERR_SHAPE, "ratio >= 1, topk >= 0 and max_blocks >= 0 are required");
+    *bound = select_bound(max_blocks, ratio, max_cache_length, q->max_prompt_length);
+    if (q->total_q * ((*bound + 15) / 16) > (int64_t(1) << 31) - 1)
+        return fail(QSA_ERR_SHAPE, "total_q * candidate blocks out of range");
+    if (*bound > kSelectMaxCandidates)
+        return fail(QSA_ERR_UNSUPPORTED, "at most %lld candidate blocks per row (min(max_blocks, (max_cache_length "
+                                         "+ max_prompt_length) / ratio) is %lld)",
+                    (long long)kSelectMaxCandidates, (long long)*bound);
+    return QSA_OK;
+}
+
+qsa_status qsa_select_blocks_workspace_size(const qsa_ragged_q *q_index, int64_t max_blocks, int64_t ratio,
+                                            int64_t topk, uint32_t max_cache_length, size_t *bytes)
+{
+    clear_error();
+    if (!bytes)
+        return fail(QSA_ERR_NULL, "bytes is NULL");
+    *bytes = 0;
+    int64_t bound;
+    qsa_status s = select_check(q_index, max_blocks, ratio, topk, max_cache_length, &bound);
+    if (s == QSA_OK)
+        *bytes = (size_t)q_index->total_q * (size_t)bound * sizeof(float);
+    return s;
+}
+
+qsa_status qsa_select_blocks(int32_t *token_indices, int64_t selection_width, int32_t *counts, int32_t *blocks,
+                             const qsa_ragged_q *q_index, const void *block_keys, int64_t max_blocks,
+                             const uint32_t *cache_lengths, uint32_t max_cache_length, int64_t ratio, int64_t topk,
+                             void *workspace, size_t workspace_bytes, void *stream)
+{
+    clear_error();
+    int64_t bound;
+    qsa_status s = select_check(q_index, max_blocks, ratio, topk, max_cache_length, &bound);
+    if (s != QSA_OK)
+        return s;
+    if (selection_width < topk * ratio + ratio - 1)
+        return fail(QSA_ERR_SHAPE, "selection_width %lld cannot hold topk * ratio + ratio - 1 = %lld positions",
+                    (long long)selection_width, (long long)(topk * ratio + ratio - 1));
+    if (q_index->total_q == 0)
+        return QSA_OK;
+    if (!token_indices || !counts || !cache_lengths || !q_index->q || (bound > 0 && !block_keys))
+        return fail(QSA_ERR_NULL, "token_indices, counts, cache_lengths, q_index and block_keys are required");
+    if (!aligned16(q_index->q) || (bound > 0 && !aligned16(block_keys)))
+        return fail(QSA_ERR_SHAPE, "q_index and block_keys must be 16-byte aligned");
+    const size_t need = (size_t)q_index->total_q * (size_t)bound * sizeof(float);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(QSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
+                    workspace ? "" : " (NULL)");
+    if (need > 0 && ((uintptr_t)workspace & 15u))
+        return fail(QSA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    SelectParams p;
+    std::memset(&p, 0, sizeof p);
+    p.token_indices = token_indices;
+    p.counts = counts;
+    p.blocks = topk > 0 ? blocks : nullptr;
+    p.q_index = q_index->q;
+    p.block_keys = block_keys;
+    p.row_off = q_index->input_row_offsets;
+    p.cache_lengths = cache_lengths;
+    p.scores = static_cast<float *>(workspace);
+    p.total_q = q_index->total_q;
+    p.width = selection_width;
+    p.max_blocks = max_blocks;
+    p.cand_bound = bound;
+    p.batch = (int32_t)q_index->batch;
+    p.dtype = q_index->dtype;
+    p.head_dim = (int32_t)q_index->head_dim;
+    p.ratio = (int32_t)ratio;
+    p.topk = (int32_t)topk;
+    const bool timed = t_ev_start && t_ev_stop;
+    int err = launch_select_blocks(p, stream, timed ? t_ev_start : nullptr, timed ? t_ev_stop : nullptr);
+    if (err)
+        return fail(QSA_ERR_HIP, "HIP launch failed: %s", hip_error_text(err));
+    return QSA_OK;
+}
+
 void qsa_set_timing_events(void *start, void *stop)
 {
     t_ev_start = start;

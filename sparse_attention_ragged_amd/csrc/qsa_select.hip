@@ -1,0 +1,323 @@
+// Block selection: the step after key compression ("QSACompressKeysPaged" names the
+// block scorer that re-derives its per-sequence stride; no page gives its contract, so
+// the rule below is this library's reading). Row r of sequence b at position pos =
+// cache_lengths[b] + (r - row_off[b]) has nfull = (pos + 1) / ratio complete blocks and
+// chooses among j < nv = min(nfull, max_blocks). Block j scores q_index[r] .
+// block_keys[b * max_blocks + j] (fp32 sum of products); the k = min(topk, nv) highest
+// scores are kept, equal scores going to the lower block index. The row's token
+// indices are the positions of the kept blocks in increasing order, then its
+// incomplete group nfull * ratio .. pos; counts[r] is their number.
+//
+// Two kernels. Scoring (HBM-bound: each block key read once per row that sees it,
+// mostly from L2 when several rows of a sequence share them) gives every block key to
+// a team of head_dim * elem / 16 lanes, one 16-byte chunk each, reduced with DPP and
+// lane shuffles; a workgroup covers consecutive blocks of one row. Selection runs one
+// workgroup per row over the row's scores held in LDS as order-preserving integer
+// keys: an MSB-first radix select (four 8-bit digit histograms with LDS atomics, one
+// histogram per wavefront) finds the k-th largest key T and how many keys equal to T
+// are needed; then each thread takes a contiguous segment of candidates, counts its
+// keys above and equal to T, and after one workgroup scan of those counts emits its
+// kept blocks at their ranks: every key above T and the first needed keys equal to T,
+// already in increasing block order.
+#include "qsa_device.hpp"
+
+namespace qsa {
+namespace {
+
+constexpr int kSelThreads = 256;
+constexpr int kScoreRounds = 4;      // blocks per team in the scoring kernel
+
+template <int DT>
+__device__ __forceinline__ float dot16(const u32x4 &a, const u32x4 &b)
+{
+    float s = 0.f;
+    if constexpr (DT == QSA_BF16) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            s += bf16_lo(a[w]) * bf16_lo(b[w]) + bf16_hi(a[w]) * bf16_hi(b[w]);
+    } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            s += __uint_as_float(a[w]) * __uint_as_float(b[w]);
+    }
+    return s;
+}
+
+// Candidate blocks of row r (and the row's sequence and position).
+__device__ __forceinline__ int64_t candidates(const SelectParams &p, int64_t r, int &b, int64_t &pos,
+                                             int64_t &nfull)
+{
+    b = find_seq_pos_wave(p.row_off, p.cache_lengths, p.batch, (uint32_t)r, pos);
+    nfull = (pos + 1) / p.ratio;
+    int64_t nv = nfull < p.max_blocks ? nfull : p.max_blocks;
+    return nv < p.cand_bound ? nv : p.cand_bound;
+}
+
+template <int DT, int TL>
+__global__ __launch_bounds__(kSelThreads) void select_score_kernel(SelectParams p)
+{
+    constexpr int EB = Elem<DT>::bytes;
+    constexpr int TPB = kSelThreads / TL;
+    const int64_t per_wg = (int64_t)TPB * kScoreRounds;
+    const int64_t wg_per_row = (p.cand_bound + per_wg - 1) / per_wg;
+    const int64_t r = blockIdx.x / wg_per_row;
+    const int64_t j0 = (int64_t)(blockIdx.x - r * wg_per_row) * per_wg + threadIdx.x / TL;
+    const int tl = threadIdx.x % TL;
+    int b;
+    int64_t pos, nfull;
+    const int64_t nv = candidates(p, r, b, pos, nfull);
+    if (j0 >= nv)
+        return;                                               // whole teams leave together
+    const u32x4 q = ldg16(static_cast<const char *>(p.q_index) + (r * p.head_dim) * EB + tl * 16);
+    const char *keys = static_cast<const char *>(p.block_keys) + ((int64_t)b * p.max_blocks * p.head_dim) * EB + tl * 16;
+    u32x4 k[kScoreRounds];
+#pragma unroll
+    for (int i = 0; i < kScoreRounds; ++i) {
+        const int64_t j = j0 + (int64_t)i * TPB;
+        k[i] = ldg16(keys + ((j < nv ? j : j0) * p.head_dim) * EB);
+    }
+#pragma unroll
+    for (int i = 0; i < kScoreRounds; ++i) {
+        const int64_t j = j0 + (int64_t)i * TPB;
+        const float s = team_sum<TL>(dot16<DT>(q, k[i]));
+        if (j < nv && tl == 0)
+            p.scores[r * p.cand_bound + j] = s;
+    }
+}
+
+// binary32 -> unsigned integer with the same order (larger float, larger key).
+__device__ __forceinline__ uint32_t order_key(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive prefix sum of v over the workgroup in thread order (wavefront scans with
+// lane shuffles, then the wavefronts' totals through LDS).
+__device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t *s_wave)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t inc = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t u = (uint32_t)__shfl_up((int)inc, off);
+        inc += lane >= off ? u : 0u;
+    }
+    if (lane == 63)
+        s_wave[wave] = inc;
+    __syncthreads();
+    uint32_t before = 0u;
+#pragma unroll
+    for (int w = 0; w < kSelThreads / 64; ++w)
+        before += w < wave ? s_wave[w] : 0u;
+    return before + inc - v;
+}
+
+template <int CAP>
+__global__ __launch_bounds__(kSelThreads) void select_topk_kernel(SelectParams p)
+{
+    constexpr int NW = kSelThreads / 64;
+    __shared__ uint32_t s_key[CAP];
+    // one histogram per wavefront during the radix select; afterwards the kept blocks
+    // in rank order (when they fit), so the outputs are written coalesced
+    constexpr int kStaged = NW * 256;
+    __shared__ uint32_t s_hist[NW][256];
+    uint32_t *s_sel = &s_hist[0][0];
+    __shared__ uint32_t s_wave[NW];
+    __shared__ uint32_t s_digit[2];                           // chosen digit, keys still needed
+    const int64_t r = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    int b;
+    int64_t pos, nfull;
+    const int64_t nv = candidates(p, r, b, pos, nfull);
+    const int64_t k = p.topk < nv ? p.topk : nv;
+    const int64_t tail = pos + 1 - nfull * p.ratio;           // 0 .. ratio - 1
+    int32_t *idx = p.token_indices + r * p.width;
+
+    // threshold: the k-th largest key T, and how many keys equal to T to keep
+    uint32_t T = 0u, need_eq = 0u;
+    const bool partial = k > 0 && k < nv;
+    if (partial) {
+        // eight loads in flight per thread (the loop is otherwise latency-bound)
+        const float *sc = p.scores + r * p.cand_bound;
+        for (int64_t i0 = 0; i0 < nv; i0 += 8 * kSelThreads) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t i = i0 + u * kSelThreads + tid;
+                v[u] = sc[i < nv ? i : 0];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t i = i0 + u * kSelThreads + tid;
+                if (i < nv)
+                    s_key[i] = order_key(v[u]);
+            }
+        }
+        uint32_t prefix = 0u, mask = 0u, remaining = (uint32_t)k;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+                s_hist[w][tid] = 0u;
+            __syncthreads();
+#pragma unroll 8
+            for (int64_t i = tid; i < nv; i += kSelThreads) {
+                const uint32_t key = s_key[i];
+                if ((key & mask) == prefix)
+                    atomicAdd(&s_hist[wave][(key >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            if (tid < 64) {
+                // lane l holds bins 4l .. 4l+3; suffix sums from the top bin down
+                uint32_t h[4], local = 0u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h[e] = 0u;
+#pragma unroll
+                    for (int w = 0; w < NW; ++w)
+                        h[e] += s_hist[w][4 * tid + e];
+                    local += h[e];
+                }
+                // inclusive suffix sum over lanes (lane l: sum of lanes l..63)
+                uint32_t suf = local;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const uint32_t v = (uint32_t)__shfl_down((int)suf, off);
+                    suf += tid + off < 64 ? v : 0u;
+                }
+                uint32_t sc = suf - local;                      // keys in bins above bin e
+#pragma unroll
+                for (int e = 3; e >= 0; --e) {
+                    if (sc < remaining && sc + h[e] >= remaining) {
+                        s_digit[0] = (uint32_t)(4 * tid + e);
+                        s_digit[1] = remaining - sc;
+                    }
+                    sc += h[e];
+                }
+            }
+            __syncthreads();
+            prefix |= s_digit[0] << shift;
+            mask |= 255u << shift;
+            remaining = s_digit[1];
+            __syncthreads();
+        }
+        T = prefix;
+        need_eq = remaining;
+    }
+
+    // keep, in block order, every key above T and the first need_eq keys equal to T (all
+    // candidates when k == nv). Thread t owns a contiguous segment of candidates: one
+    // count pass, one workgroup scan of its (above, equal) counts, one emitting pass.
+    if (k > 0) {
+        // an odd segment length keeps the threads' LDS reads on distinct banks
+        const int64_t seg = ((nv + kSelThreads - 1) / kSelThreads) | 1;
+        const int64_t lo = tid * seg < nv ? tid * seg : nv;
+        const int64_t hi = lo + seg < nv ? lo + seg : nv;
+        uint32_t gt = 0u, eq = 0u;
+        if (partial) {
+#pragma unroll 8
+            for (int64_t i = lo; i < hi; ++i) {
+                const uint32_t key = s_key[i];
+                gt += key > T ? 1u : 0u;
+                eq += key == T ? 1u : 0u;
+            }
+        }
+        // both counts fit 16 bits (at most 32768 candidates): scan them packed
+        const uint32_t before = block_exclusive_sum((gt << 16) | eq, s_wave);
+        uint32_t eq_seen = before & 0xffffu;
+        int64_t m = partial ? (int64_t)(before >> 16) + (eq_seen < need_eq ? eq_seen : need_eq) : lo;
+        const bool staged = k <= kStaged;
+        for (int64_t i = lo; i < hi; ++i) {
+            bool sel = true;
+            if (partial) {
+                const uint32_t key = s_key[i];
+                sel = key > T || (key == T && eq_seen < need_eq);
+                eq_seen += key == T ? 1u : 0u;
+            }
+            if (sel) {
+                if (staged) {
+                    s_sel[m] = (uint32_t)i;
+                } else {
+                    for (int t = 0; t < p.ratio; ++t)
+                        idx[m * p.ratio + t] = (int32_t)(i * p.ratio + t);
+                    if (p.blocks)
+                        p.blocks[r * p.topk + m] = (int32_t)i;
+                }
+                ++m;
+            }
+        }
+        if (staged) {
+            __syncthreads();
+            for (int64_t e = tid; e < k * p.ratio; e += kSelThreads) {
+                const int64_t q = e / p.ratio;
+                idx[e] = (int32_t)((int64_t)s_sel[q] * p.ratio + (e - q * p.ratio));
+            }
+            if (p.blocks)
+                for (int64_t q = tid; q < k; q += kSelThreads)
+                    p.blocks[r * p.topk + q] = (int32_t)s_sel[q];
+        }
+    }
+    // the incomplete group, the count, and -1 for unused block slots
+    for (int64_t t = tid; t < tail; t += kSelThreads)
+        idx[k * p.ratio + t] = (int32_t)(nfull * p.ratio + t);
+    if (tid == 0)
+        p.counts[r] = (int32_t)(k * p.ratio + tail);
+    if (p.blocks)
+        for (int64_t m = k + tid; m < p.topk; m += kSelThreads)
+            p.blocks[r * p.topk + m] = -1;
+}
+
+template <int DT>
+int launch_score(const SelectParams &p, hipStream_t s)
+{
+    const int tl = p.head_dim * Elem<DT>::bytes / 16;
+    const int64_t per_wg = (int64_t)(kSelThreads / tl) * kScoreRounds;
+    const dim3 grid((unsigned)(p.total_q * ((p.cand_bound + per_wg - 1) / per_wg))), block(kSelThreads);
+    switch (tl) {
+    case 1: hipLaunchKernelGGL((select_score_kernel<DT, 1>), grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((select_score_kernel<DT, 2>), grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((select_score_kernel<DT, 4>), grid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL((select_score_kernel<DT, 8>), grid, block, 0, s, p); break;
+    case 16: hipLaunchKernelGGL((select_score_kernel<DT, 16>), grid, block, 0, s, p); break;
+    case 32: hipLaunchKernelGGL((select_score_kernel<DT, 32>), grid, block, 0, s, p); break;
+    case 64: hipLaunchKernelGGL((select_score_kernel<DT, 64>), grid, block, 0, s, p); break;
+    default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}
+
+}  // namespace
+
+bool select_supported(int32_t dtype, int32_t head_dim)
+{
+    if (dtype != QSA_F32 && dtype != QSA_BF16)
+        return false;
+    const int64_t bytes = (int64_t)head_dim * (dtype == QSA_F32 ? 4 : 2);
+    return bytes >= 16 && bytes <= 1024 && ((bytes / 16) & (bytes / 16 - 1)) == 0 && bytes % 16 == 0;
+}
+
+int launch_select_blocks(const SelectParams &p, void *stream, void *ev_start, void *ev_stop)
+{
+    if (p.total_q == 0)
+        return 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int err = 0;
+    if (ev_start)
+        err = (int)hipEventRecord(static_cast<hipEvent_t>(ev_start), s);
+    if (!err && p.cand_bound > 0)
+        err = p.dtype == QSA_BF16 ? launch_score<QSA_BF16>(p, s) : launch_score<QSA_F32>(p, s);
+    if (!err) {
+        const dim3 grid((unsigned)p.total_q), block(kSelThreads);
+        if (p.cand_bound <= 4096)
+            hipLaunchKernelGGL(select_topk_kernel<4096>, grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL(select_topk_kernel<kSelectMaxCandidates>, grid, block, 0, s, p);
+        err = (int)hipGetLastError();
+    }
+    if (!err && ev_stop)
+        err = (int)hipEventRecord(static_cast<hipEvent_t>(ev_stop), s);
+    return err;
+}
+
+}  // namespace qsa

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(qsa):
 
 
 def test_abi_version_and_struct_sizes(qsa):
-    assert qsa.lib.qsa_abi_version() == 3
+    assert qsa.lib.qsa_abi_version() == 4
     assert qsa.lib.qsa_struct_size(0) == ctypes.sizeof(qsa._Cache) == 104
     assert qsa.lib.qsa_struct_size(1) == ctypes.sizeof(qsa._Ragged) == 64
     assert qsa.lib.qsa_struct_size(2) == ctypes.sizeof(qsa.LaunchOptions) == 16
@@ -250,3 +250,36 @@ def test_compress_keys_checks(qsa):
     assert call(batch=0) == 0
     assert call(max_blocks=0) == 0
     assert call(kv=cache(num_kv_heads=1, max_cache_length=2, max_pages=4, page_size=16), mpl=1) == 0  # 3 / 4 = 0
+
+
+def test_select_blocks_checks(qsa):
+    """Block selection: bad arguments are refused on the host before any launch; zero
+    rows return OK without launching."""
+    f = qsa.lib.qsa_select_blocks
+    n = ctypes.c_size_t(0)
+
+    def q(**kw):
+        d = dict(num_q_heads=1, head_dim=128, max_prompt_length=1)
+        d.update(kw)
+        return ragged(**d)
+
+    def call(qd=None, W=2051, idx=P, counts=P, blocks=P, keys=P, max_blocks=64, cl=P, mcl=1000, ratio=4, topk=512,
+             ws=P, wsb=1 << 30):
+        qd = qd or q()
+        return f(idx, W, counts, blocks, ctypes.byref(qd), keys, max_blocks, cl, mcl, ratio, topk, ws, wsb, None)
+
+    assert call(qd=q(num_q_heads=2)) == 2                            # one index query per row
+    assert call(qd=q(dtype=2)) == 3                                  # e4m3 not offered
+    assert call(qd=q(head_dim=96)) == 4                              # 192-byte rows not built
+    assert call(ratio=0) == 2 and call(topk=-1) == 2 and call(max_blocks=-1) == 2
+    assert call(W=2050) == 2 and "selection_width" in msg(qsa)      # 512 * 4 + 3 positions
+    assert call(max_blocks=40000, mcl=0, qd=q(max_prompt_length=0)) == 4    # over 32768 candidates
+    assert call(idx=0) == 1 and call(counts=0) == 1 and call(cl=0) == 1 and call(keys=0) == 1
+    assert call(keys=P + 4) == 2
+    assert call(ws=0) == 5 and call(wsb=16) == 5 and call(ws=P + 8) == 5
+    # workspace: fp32 scores for min(max_blocks, (1000 + 1) / 4) = 64 candidates of 3 rows
+    assert qsa.lib.qsa_select_blocks_workspace_size(ctypes.byref(q()), 64, 4, 512, 1000, ctypes.byref(n)) == 0
+    assert n.value == 3 * 64 * 4
+    assert qsa.lib.qsa_select_blocks_workspace_size(ctypes.byref(q()), 640, 4, 512, 1000, ctypes.byref(n)) == 0
+    assert n.value == 3 * 250 * 4
+    assert call(qd=q(total_q=0)) == 0                                # nothing to do

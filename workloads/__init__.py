@@ -648,6 +648,17 @@ def f2_compress_keys_bf16(seed=9, batch=32, cache_range=(16384, 32768)):
                          ratio=4, rotary_dim=64, eps=1e-6)
 
 
+def f4_select_blocks_bf16(seed=10, batch=32, cache_range=(16384, 32768), topk=511):
+    """Block selection at the indexer workload's shapes: one decode row per sequence
+    (cache lengths U[16k, 32k]), blocks of 4 positions (4k-8k candidates per row), one
+    bf16 index query of 128 channels per row, top 511 blocks into 511 * 4 + 3 = 2047
+    positions."""
+    rng = np.random.default_rng(seed + 10_000)
+    cl = rng.integers(cache_range[0], cache_range[1], size=batch, endpoint=True)
+    return make_select(name="f4_select_blocks_bf16", seed=seed, rows=[1] * batch, cache_lengths=cl, head_dim=128,
+                       dtype="bf16", ratio=4, topk=topk)
+
+
 NAMED = {
     "c1_tiny_fp32": c1_tiny_fp32,
     "c2_decode_bf16": c2_decode_bf16,
@@ -658,6 +669,7 @@ NAMED = {
     "c5_latent_bf16": c5_latent_bf16,
     "f3_dense_prefill_bf16": f3_dense_prefill_bf16,
     "f2_compress_keys_bf16": f2_compress_keys_bf16,
+    "f4_select_blocks_bf16": f4_select_blocks_bf16,
 }
 
 

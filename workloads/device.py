@@ -129,3 +129,29 @@ def run_compress(dc: DeviceCompress, out=None, stream=None) -> torch.Tensor:
     return qsa.compress_keys(dc.kv, dc.key_counts, dc.gamma, dc.freqs, c.layer_idx, c.ratio, c.rotary_dim, c.eps,
                              max_blocks=c.max_blocks, max_prompt_length=c.max_prompt_length, out=out,
                              stream=stream)
+
+
+@dataclass
+class DeviceSelect:
+    case: object
+    q_index: torch.Tensor
+    block_keys: torch.Tensor
+    row_off: torch.Tensor
+    cache_lengths: torch.Tensor
+
+
+def select_to_device(case, device="cuda") -> DeviceSelect:
+    """Device copies of a ``workloads.SelectCase``."""
+    return DeviceSelect(case=case, q_index=case.q_index.to(device).contiguous(),
+                        block_keys=case.block_keys.to(device).contiguous(),
+                        row_off=_i32(case.input_row_offsets, device), cache_lengths=_i32(case.cache_lengths, device))
+
+
+def run_select(dc: DeviceSelect, token_indices=None, counts=None, blocks=None, workspace=None, stream=None):
+    """One block-selection call; returns (token_indices, counts, blocks)."""
+    import sparse_attention_ragged_amd as qsa
+    c = dc.case
+    return qsa.select_blocks(dc.q_index, dc.row_off, dc.block_keys, dc.cache_lengths, c.max_blocks, c.ratio, c.topk,
+                             selection_width=c.W, max_cache_length=int(np.max(c.cache_lengths)) if c.batch else 0,
+                             max_prompt_length=c.max_prompt_length, token_indices=token_indices, counts=counts,
+                             blocks=blocks, workspace=workspace, stream=stream)
