@@ -6,6 +6,7 @@
 #include <cstring>
 
 #include "qsa_host.hpp"
+#include "qsa_select_host.hpp"
 
 namespace qsa {
 const char *last_error_text();

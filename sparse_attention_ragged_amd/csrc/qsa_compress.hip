@@ -19,6 +19,7 @@
 // once; other ratios loop over the group four rows at a time. No LDS, no barriers: a
 // team whose block does not exist leaves at once.
 #include "qsa_device.hpp"
+#include "qsa_select_host.hpp"
 
 namespace qsa {
 namespace {

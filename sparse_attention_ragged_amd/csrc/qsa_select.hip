@@ -20,6 +20,7 @@
 // kept blocks at their ranks: every key above T and the first needed keys equal to T,
 // already in increasing block order.
 #include "qsa_device.hpp"
+#include "qsa_select_host.hpp"
 
 namespace qsa {
 namespace {
