@@ -7,6 +7,7 @@
 
 #include "qsa_host.hpp"
 #include "qsa_select_host.hpp"
+#include "qsa_flash_host.hpp"
 
 namespace qsa {
 const char *last_error_text();
@@ -386,6 +387,23 @@ qsa_status qsa_ragged_attention(void *out, int32_t out_dtype, const qsa_ragged_q
     p.dense_v = v;
     p.dense_causal = causal;
     p.window = window > 0 ? window : 0;
+    // matrix-core groups without a split: workgroups of consecutive rows share key tiles
+    // (unless a launch option asks for a wavefront count, which only the per-row kernel takes)
+    if (plan.path == PATH_MFMA && plan.num_splits == 1 && plan.schedule == SCHED_STATIC &&
+        (!opts || opts->waves == 0) && mfma_flash_supported(q->dtype, p.group, p.head_dim)) {
+        if (q->total_q == 0)
+            return QSA_OK;
+        int err = 0;
+        if (t_ev_start && t_ev_stop)
+            err = record_event(t_ev_start, stream);
+        if (!err)
+            err = launch_gather_mfma_flash(p, stream);
+        if (!err && t_ev_start && t_ev_stop)
+            err = record_event(t_ev_stop, stream);
+        if (err)
+            return fail(QSA_ERR_HIP, "HIP launch failed: %s", hip_error_text(err));
+        return QSA_OK;
+    }
     return run(p, plan, stream);
 }
 

@@ -83,3 +83,26 @@ def test_dense_prefill_c3_shapes_sampled_rows():
     announce("dense prefill c3 shapes (%d rows checked)" % len(rows))
     got, ref, _ = run(case, rows=rows)
     compare(got, ref, "bf16", "dense prefill", rel_rms_max=0.01)
+
+
+@pytest.mark.parametrize("causal,window", [(True, -1), (False, -1), (True, 3), (False, 2)])
+def test_dense_shared_tiles_across_short_sequences(causal, window):
+    """Matrix-core groups without a split run four consecutive rows per workgroup over
+    their shared key tiles; with many short sequences a workgroup's rows straddle
+    sequence boundaries (the union of their key ranges is still contiguous) and each row
+    must mask the other sequences' keys."""
+    case = dense(85, [1, 2, 3, 1, 5, 7, 0, 4, 33, 1, 6], 2, 16, 128, "bf16", causal=causal, window=window)
+    announce("dense short sequences causal=%s window=%d" % (causal, window))
+    got, ref, _ = run(case)
+    compare(got, ref, "bf16", "dense short sequences")
+
+
+def test_dense_per_row_kernel_matches_shared_tiles():
+    """The per-row matrix-core kernel (taken when a wavefront count is requested) and the
+    shared-tile kernel (the automatic choice) both match the oracle."""
+    case = dense(86, [300, 45, 129], 2, 16, 128, "bf16", causal=True)
+    announce("dense per-row vs shared tiles")
+    got_auto, ref, dc = run(case)
+    got_rows, _, _ = run(case, options={"waves": 4})
+    compare(got_auto, ref, "bf16", "dense shared tiles")
+    compare(got_rows, ref, "bf16", "dense per-row")
