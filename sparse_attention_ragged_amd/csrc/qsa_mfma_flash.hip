@@ -241,29 +241,28 @@ gather_mfma_flash_kernel(GatherParams p)
     };
 
     // two tiles in flight: tile t + 2 is loaded while tile t is consumed and tile t + 1
-    // (loaded one iteration earlier) goes to the other LDS buffer; one barrier per tile
+    // (loaded one iteration earlier) goes to the other LDS buffer; one barrier per tile.
+    // Loads and stores are unconditional (a tile past the range reads the range's first
+    // rows and is never consumed), and every trip starts with the same two register sets
+    // in flight, so the compiler's wait counts keep the newer tile's loads in flight
+    // instead of draining them.
     if (nt > 0) {
         Rows R0, R1;
         load_tile(0, R0);
-        if (nt > 1)
-            load_tile(1, R1);
-        store_tile(0, R0);
-        lds_barrier();
-        for (int t = 0; t < nt; t += 2) {
-            if (t + 2 < nt)
-                load_tile(t + 2, R0);
+        load_tile(1, R1);
+        for (int t = 0;; t += 2) {
+            store_tile(0, R0);                    // tile t
+            lds_barrier();
+            load_tile(t + 2, R0);
             consume(t, 0);
-            if (t + 1 < nt)
-                store_tile(1, R1);
+            store_tile(1, R1);                    // tile t + 1
             lds_barrier();
             if (t + 1 >= nt)
                 break;
-            if (t + 3 < nt)
-                load_tile(t + 3, R1);
+            load_tile(t + 3, R1);
             consume(t + 1, 1);
-            if (t + 2 < nt)
-                store_tile(0, R0);
-            lds_barrier();
+            if (t + 2 >= nt)
+                break;
         }
     }
 
