@@ -164,3 +164,42 @@ def test_chain_compress_select_attend():
     out = D.run(datt)
     torch.cuda.synchronize()
     compare(out, oracle.run_case(att), "bf16", "chain attention")
+
+
+def test_select_graph_replays_match_eager():
+    """Captured in a HIP graph with a caller-provided workspace (no allocation, no
+    memset): every replay, with eager work in between, reproduces the eager call."""
+    import sparse_attention_ragged_amd as qsa
+    case = W.make_select(name="sel_graph", seed=77, rows=[1, 3, 2], cache_lengths=[900, 300, 5000], head_dim=128,
+                         dtype="bf16", ratio=4, topk=50, integer=True)
+    dc = D.select_to_device(case, DEV)
+    n = qsa.select_blocks_workspace_size(dc.q_index, dc.row_off, case.max_blocks, case.ratio, case.topk,
+                                         int(np.max(case.cache_lengths)), case.max_prompt_length)
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    idx = torch.full((case.total_q, case.W), FILL, dtype=torch.int32, device=DEV)
+    counts = torch.zeros(case.total_q, dtype=torch.int32, device=DEV)
+    blocks = torch.zeros((case.total_q, case.topk), dtype=torch.int32, device=DEV)
+    announce("select graph: eager")
+    D.run_select(dc, token_indices=idx, counts=counts, blocks=blocks, workspace=ws)
+    torch.cuda.synchronize()
+    eager = (idx.clone(), counts.clone(), blocks.clone())
+    check_exact(case, (eager[0].cpu().numpy(), eager[1].cpu().numpy(), eager[2].cpu().numpy()), "select graph eager")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            D.run_select(dc, token_indices=idx, counts=counts, blocks=blocks, workspace=ws, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for k in range(4):
+        announce("select graph: replay %d" % k)
+        idx.fill_(FILL)
+        counts.zero_()
+        blocks.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, eager[0]) and torch.equal(counts, eager[1]) and torch.equal(blocks, eager[2]), \
+            "replay %d differs from the eager call" % k
+    del g
