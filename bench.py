@@ -50,12 +50,22 @@ GATHER_SOURCES = ("sparse_attention_ragged_amd/csrc/qsa_valu.hip", "sparse_atten
                   "sparse_attention_ragged_amd/csrc/qsa_plan.cpp", "include/qsa.h")
 
 
+def _code_only(text):
+    """C/C++ source without comments and whitespace: documentation edits leave the
+    code (and so the kernel) unchanged."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return re.sub(r"\s+", "", text)
+
+
 def csrc_digest():
-    """sha256 over the gather kernel's sources (names and contents, in a fixed order)."""
+    """sha256 over the gather kernel's sources (names and code without comments, in a
+    fixed order)."""
     h = hashlib.sha256()
     for name in GATHER_SOURCES:
         h.update(name.encode())
-        h.update(open(os.path.join(ROOT, name), "rb").read())
+        h.update(_code_only(open(os.path.join(ROOT, name), encoding="utf-8").read()).encode())
     return h.hexdigest()
 
 

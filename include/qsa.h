@@ -14,7 +14,10 @@
  *   qsa_latent_sparse_attention  one shared latent head: sliding-window keys plus
  *                                listed compressed entries plus a per-head sink logit
  *                                ("latent_sparse_attention_ragged_paged", summary,
- *                                Parameters and Args).
+ *                                Parameters and Args);
+ *   qsa_ragged_attention         dense causal / sliding-window / unmasked attention
+ *                                over ragged q, k, v without a cache
+ *                                ("RaggedFlashAttentionGPU", summary, Parameters and Args);
  *
  * and the steps that produce a selection: the key compression that pools raw index
  * keys into block keys (qsa_compress_keys, "QSACompressKeysPaged") and the top-k block
@@ -22,7 +25,8 @@
  *
  * Conventions shared by every entry point:
  *   - Pointers are DEVICE pointers unless a comment says (host). The caller owns
- *     every buffer; the library writes only `out` and `workspace`, never
+ *     every buffer; the library writes only the call's output buffers (`out`,
+ *     `block_keys`, `token_indices`, `counts`, `blocks`) and `workspace`, never
  *     allocates, frees or synchronises, and reads no device data on the host.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).
  *   - Workspace: the size the matching *_workspace_size call reports, 16-byte
