@@ -140,17 +140,18 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(SelectParams p
     uint32_t T = 0u, need_eq = 0u;
     const bool partial = k > 0 && k < nv;
     if (partial) {
-        // eight loads in flight per thread (the loop is otherwise latency-bound)
+        // sixteen loads in flight per thread (the loop is otherwise latency-bound)
+        constexpr int kInFlight = 16;
         const float *sc = p.scores + r * p.cand_bound;
-        for (int64_t i0 = 0; i0 < nv; i0 += 8 * kSelThreads) {
-            float v[8];
+        for (int64_t i0 = 0; i0 < nv; i0 += kInFlight * kSelThreads) {
+            float v[kInFlight];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < kInFlight; ++u) {
                 const int64_t i = i0 + u * kSelThreads + tid;
                 v[u] = sc[i < nv ? i : 0];
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < kInFlight; ++u) {
                 const int64_t i = i0 + u * kSelThreads + tid;
                 if (i < nv)
                     s_key[i] = order_key(v[u]);
