@@ -13,12 +13,13 @@
 // a team of head_dim * elem / 16 lanes, one 16-byte chunk each, reduced with DPP and
 // lane shuffles; a workgroup covers consecutive blocks of one row. Selection runs one
 // workgroup per row over the row's scores held in LDS as order-preserving integer
-// keys: an MSB-first radix select (four 8-bit digit histograms with LDS atomics, one
-// histogram per wavefront) finds the k-th largest key T and how many keys equal to T
+// keys: an MSB-first radix select (up to four 8-bit digit histograms with LDS atomics,
+// one histogram per wavefront; it stops once every key left in the chosen bin is
+// needed) finds the high bits of the k-th largest key and how many keys sharing them
 // are needed; then each thread takes a contiguous segment of candidates, counts its
-// keys above and equal to T, and after one workgroup scan of those counts emits its
-// kept blocks at their ranks: every key above T and the first needed keys equal to T,
-// already in increasing block order.
+// keys above that bin and in it, and after one workgroup scan of those counts emits
+// its kept blocks at their ranks: every key above the bin and the first needed keys
+// in it, already in increasing block order.
 #include "qsa_device.hpp"
 #include "qsa_select_host.hpp"
 
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(SelectParams p
     __shared__ uint32_t s_hist[NW][256];
     uint32_t *s_sel = &s_hist[0][0];
     __shared__ uint32_t s_wave[NW];
-    __shared__ uint32_t s_digit[2];                           // chosen digit, keys still needed
+    __shared__ uint32_t s_digit[3];                           // chosen digit, keys still needed, keys in its bin
     const int64_t r = blockIdx.x;
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -136,8 +137,10 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(SelectParams p
     const int64_t tail = pos + 1 - nfull * p.ratio;           // 0 .. ratio - 1
     int32_t *idx = p.token_indices + r * p.width;
 
-    // threshold: the k-th largest key T, and how many keys equal to T to keep
-    uint32_t T = 0u, need_eq = 0u;
+    // threshold: the resolved high bits (prefix P under mask M) of the k-th largest key
+    // and how many keys with those bits to keep. The passes stop early once every key
+    // left in the chosen bin is needed.
+    uint32_t P = 0u, M = 0u, need_eq = 0u;
     const bool partial = k > 0 && k < nv;
     if (partial) {
         // sixteen loads in flight per thread (the loop is otherwise latency-bound)
@@ -194,6 +197,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(SelectParams p
                     if (sc < remaining && sc + h[e] >= remaining) {
                         s_digit[0] = (uint32_t)(4 * tid + e);
                         s_digit[1] = remaining - sc;
+                        s_digit[2] = h[e];
                     }
                     sc += h[e];
                 }
@@ -202,9 +206,13 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(SelectParams p
             prefix |= s_digit[0] << shift;
             mask |= 255u << shift;
             remaining = s_digit[1];
+            const bool all_of_bin = s_digit[2] == remaining;
             __syncthreads();
+            if (all_of_bin)
+                break;                            // every key with this prefix is kept
         }
-        T = prefix;
+        P = prefix;
+        M = mask;
         need_eq = remaining;
     }
 
@@ -221,8 +229,8 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(SelectParams p
 #pragma unroll 8
             for (int64_t i = lo; i < hi; ++i) {
                 const uint32_t key = s_key[i];
-                gt += key > T ? 1u : 0u;
-                eq += key == T ? 1u : 0u;
+                gt += key > (P | ~M) ? 1u : 0u;
+                eq += (key & M) == P ? 1u : 0u;
             }
         }
         // both counts fit 16 bits (at most 32768 candidates): scan them packed
@@ -234,8 +242,9 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(SelectParams p
             bool sel = true;
             if (partial) {
                 const uint32_t key = s_key[i];
-                sel = key > T || (key == T && eq_seen < need_eq);
-                eq_seen += key == T ? 1u : 0u;
+                const bool eq = (key & M) == P;
+                sel = key > (P | ~M) || (eq && eq_seen < need_eq);
+                eq_seen += eq ? 1u : 0u;
             }
             if (sel) {
                 if (staged) {
