@@ -205,11 +205,12 @@ gather_mfma_kernel(GatherParams p)
             R.v[i] = ldg16(rok ? kaddr + vdelta : dummy + my_chunk * 16);
         }
     };
-    auto consume = [&](const Rows &R) {
-        const uint32_t present = R.present;
-        // rows -> the wavefront's LDS tiles (V widened to bf16); LDS operations of one
-        // wavefront execute in order, the empty asm statements keep the compiler from
-        // moving the accesses across each other
+    uint32_t present = 0u;                       // keys present in the staged tile
+    // rows -> the wavefront's LDS tiles (V widened to bf16); LDS operations of one
+    // wavefront execute in order, the empty asm statements keep the compiler from
+    // moving the accesses across each other (the previous tile's reads come first)
+    auto stage = [&](const Rows &R) {
+        present = R.present;
         asm volatile("" ::: "memory");
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
@@ -225,6 +226,8 @@ gather_mfma_kernel(GatherParams p)
             }
         }
         asm volatile("" ::: "memory");
+    };
+    auto compute = [&]() {
         // S^T (two 16-key halves); A = 8 dims of key 16h + i from the K tile
         f32x4_t st[2];
 #pragma unroll
@@ -291,31 +294,35 @@ gather_mfma_kernel(GatherParams p)
         asm volatile("" ::: "memory");
     };
 
+    // One register set of rows: tile i is copied to the wavefront's LDS tile as soon as
+    // it has arrived, then tile i + 1's rows are issued into the same registers and
+    // tile i is computed from LDS while they are in flight. Every trip starts with
+    // entries i + 2, pages i + 1 and rows i in flight.
     if (nb > 0) {
         Entries E0, E1;
         Pages P0, P1;
-        Rows R0, R1;
+        Rows R;
         load_entries(0, E0);
         load_entries(1, E1);
         load_pages(0, E0, P0);
         load_entries(2, E0);
         load_pages(1, E1, P1);
-        load_rows(P0, R0);
-        load_entries(3, E1);
-        load_pages(2, E0, P0);
-        load_rows(P1, R1);
-        consume(R0);
-        for (int i = 2; i <= nb; i += 2) {
-            load_entries(i + 2, E0);
-            load_pages(i + 1, E1, P1);
-            load_rows(P0, R0);
-            consume(R1);
-            if (i + 1 > nb)
-                break;
+        load_rows(P0, R);
+        for (int i = 0;; i += 2) {
+            stage(R);                            // rows i
+            load_rows(P1, R);                    // rows i + 1
             load_entries(i + 3, E1);
             load_pages(i + 2, E0, P0);
-            load_rows(P1, R1);
-            consume(R0);
+            compute();                           // tile i
+            if (i + 1 >= nb)
+                break;
+            stage(R);                            // rows i + 1
+            load_rows(P0, R);                    // rows i + 2
+            load_entries(i + 4, E0);
+            load_pages(i + 3, E1, P1);
+            compute();                           // tile i + 1
+            if (i + 2 >= nb)
+                break;
         }
     }
 
