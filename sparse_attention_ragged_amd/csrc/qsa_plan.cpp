@@ -230,7 +230,9 @@ qsa_status plan_gather(const qsa_ragged_q *q, int64_t num_kv_heads, int32_t dtyp
         // the matrix-core kernel gives each wavefront its own (row, kv head, split)
         const int64_t target = plan->path == PATH_MFMA ? kTargetWorkgroups * (plan->waves < 4 ? plan->waves : 4)
                                                        : kTargetWorkgroups;
-        splits = items > 0 ? ceil_div(target, items) : 1;
+        // matrix-core wavefronts: round down, so that every item stays resident (two
+        // workgroups per CU); a few items over that would run as a short second round
+        splits = items > 0 ? (plan->path == PATH_MFMA ? target / items : ceil_div(target, items)) : 1;
         int64_t by_len = ceil_div(cap, kMinKeysPerSplit);
         if (splits > by_len)
             splits = by_len;
