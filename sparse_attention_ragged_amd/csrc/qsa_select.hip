@@ -26,7 +26,8 @@
 namespace qsa {
 namespace {
 
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 256;    // scoring kernel
+constexpr int kTopkThreads = 1024;  // selection kernel: sixteen wavefronts hide its LDS latency
 constexpr int kScoreRounds = 4;      // blocks per team in the scoring kernel
 
 template <int DT>
@@ -94,8 +95,9 @@ __device__ __forceinline__ uint32_t order_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum of v over the workgroup in thread order (wavefront scans with
-// lane shuffles, then the wavefronts' totals through LDS).
+// Exclusive prefix sum of v over a workgroup of TH threads in thread order (wavefront
+// scans with lane shuffles, then the wavefronts' totals through LDS).
+template <int TH>
 __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t *s_wave)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -110,20 +112,22 @@ __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t *s_
     __syncthreads();
     uint32_t before = 0u;
 #pragma unroll
-    for (int w = 0; w < kSelThreads / 64; ++w)
+    for (int w = 0; w < TH / 64; ++w)
         before += w < wave ? s_wave[w] : 0u;
     return before + inc - v;
 }
 
 template <int CAP>
-__global__ __launch_bounds__(kSelThreads) void select_topk_kernel(SelectParams p)
+__global__ __launch_bounds__(kTopkThreads) void select_topk_kernel(SelectParams p)
 {
-    constexpr int NW = kSelThreads / 64;
+    constexpr int TH = kTopkThreads;
+    constexpr int NW = TH / 64;
     __shared__ uint32_t s_key[CAP];
     // one histogram per wavefront during the radix select; afterwards the kept blocks
     // in rank order (when they fit), so the outputs are written coalesced
     constexpr int kStaged = NW * 256;
     __shared__ uint32_t s_hist[NW][256];
+    __shared__ uint32_t s_bin[256];                           // the wavefronts' histograms summed
     uint32_t *s_sel = &s_hist[0][0];
     __shared__ uint32_t s_wave[NW];
     __shared__ uint32_t s_digit[3];                           // chosen digit, keys still needed, keys in its bin
@@ -143,34 +147,41 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(SelectParams p
     uint32_t P = 0u, M = 0u, need_eq = 0u;
     const bool partial = k > 0 && k < nv;
     if (partial) {
-        // sixteen loads in flight per thread (the loop is otherwise latency-bound)
-        constexpr int kInFlight = 16;
+        // eight loads in flight per thread (the loop is otherwise latency-bound)
+        constexpr int kInFlight = 8;
         const float *sc = p.scores + r * p.cand_bound;
-        for (int64_t i0 = 0; i0 < nv; i0 += kInFlight * kSelThreads) {
+        for (int64_t i0 = 0; i0 < nv; i0 += kInFlight * TH) {
             float v[kInFlight];
 #pragma unroll
             for (int u = 0; u < kInFlight; ++u) {
-                const int64_t i = i0 + u * kSelThreads + tid;
+                const int64_t i = i0 + u * TH + tid;
                 v[u] = sc[i < nv ? i : 0];
             }
 #pragma unroll
             for (int u = 0; u < kInFlight; ++u) {
-                const int64_t i = i0 + u * kSelThreads + tid;
+                const int64_t i = i0 + u * TH + tid;
                 if (i < nv)
                     s_key[i] = order_key(v[u]);
             }
         }
         uint32_t prefix = 0u, mask = 0u, remaining = (uint32_t)k;
         for (int shift = 24; shift >= 0; shift -= 8) {
-#pragma unroll
-            for (int w = 0; w < NW; ++w)
-                s_hist[w][tid] = 0u;
+            for (int i = tid; i < NW * 256; i += TH)
+                (&s_hist[0][0])[i] = 0u;
             __syncthreads();
 #pragma unroll 8
-            for (int64_t i = tid; i < nv; i += kSelThreads) {
+            for (int64_t i = tid; i < nv; i += TH) {
                 const uint32_t key = s_key[i];
                 if ((key & mask) == prefix)
                     atomicAdd(&s_hist[wave][(key >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            if (tid < 256) {
+                uint32_t h = 0u;
+#pragma unroll
+                for (int w = 0; w < NW; ++w)
+                    h += s_hist[w][tid];
+                s_bin[tid] = h;
             }
             __syncthreads();
             if (tid < 64) {
@@ -178,10 +189,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(SelectParams p
                 uint32_t h[4], local = 0u;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    h[e] = 0u;
-#pragma unroll
-                    for (int w = 0; w < NW; ++w)
-                        h[e] += s_hist[w][4 * tid + e];
+                    h[e] = s_bin[4 * tid + e];
                     local += h[e];
                 }
                 // inclusive suffix sum over lanes (lane l: sum of lanes l..63)
@@ -221,7 +229,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(SelectParams p
     // count pass, one workgroup scan of its (above, equal) counts, one emitting pass.
     if (k > 0) {
         // an odd segment length keeps the threads' LDS reads on distinct banks
-        const int64_t seg = ((nv + kSelThreads - 1) / kSelThreads) | 1;
+        const int64_t seg = ((nv + TH - 1) / TH) | 1;
         const int64_t lo = tid * seg < nv ? tid * seg : nv;
         const int64_t hi = lo + seg < nv ? lo + seg : nv;
         uint32_t gt = 0u, eq = 0u;
@@ -234,7 +242,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(SelectParams p
             }
         }
         // both counts fit 16 bits (at most 32768 candidates): scan them packed
-        const uint32_t before = block_exclusive_sum((gt << 16) | eq, s_wave);
+        const uint32_t before = block_exclusive_sum<TH>((gt << 16) | eq, s_wave);
         uint32_t eq_seen = before & 0xffffu;
         int64_t m = partial ? (int64_t)(before >> 16) + (eq_seen < need_eq ? eq_seen : need_eq) : lo;
         const bool staged = k <= kStaged;
@@ -260,22 +268,24 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(SelectParams p
         }
         if (staged) {
             __syncthreads();
-            for (int64_t e = tid; e < k * p.ratio; e += kSelThreads) {
-                const int64_t q = e / p.ratio;
-                idx[e] = (int32_t)((int64_t)s_sel[q] * p.ratio + (e - q * p.ratio));
+            // k * ratio <= pos + 1: token positions, which the int32 outputs hold
+            const uint32_t ratio = (uint32_t)p.ratio;
+            for (uint32_t e = tid; e < (uint32_t)(k * p.ratio); e += TH) {
+                const uint32_t q = e / ratio;
+                idx[e] = (int32_t)(s_sel[q] * ratio + (e - q * ratio));
             }
             if (p.blocks)
-                for (int64_t q = tid; q < k; q += kSelThreads)
+                for (int64_t q = tid; q < k; q += TH)
                     p.blocks[r * p.topk + q] = (int32_t)s_sel[q];
         }
     }
     // the incomplete group, the count, and -1 for unused block slots
-    for (int64_t t = tid; t < tail; t += kSelThreads)
+    for (int64_t t = tid; t < tail; t += TH)
         idx[k * p.ratio + t] = (int32_t)(nfull * p.ratio + t);
     if (tid == 0)
         p.counts[r] = (int32_t)(k * p.ratio + tail);
     if (p.blocks)
-        for (int64_t m = k + tid; m < p.topk; m += kSelThreads)
+        for (int64_t m = k + tid; m < p.topk; m += TH)
             p.blocks[r * p.topk + m] = -1;
 }
 
@@ -319,7 +329,7 @@ int launch_select_blocks(const SelectParams &p, void *stream, void *ev_start, vo
     if (!err && p.cand_bound > 0)
         err = p.dtype == QSA_BF16 ? launch_score<QSA_BF16>(p, s) : launch_score<QSA_F32>(p, s);
     if (!err) {
-        const dim3 grid((unsigned)p.total_q), block(kSelThreads);
+        const dim3 grid((unsigned)p.total_q), block(kTopkThreads);
         if (p.cand_bound <= 4096)
             hipLaunchKernelGGL(select_topk_kernel<4096>, grid, block, 0, s, p);
         else
