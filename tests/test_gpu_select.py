@@ -92,6 +92,9 @@ EXACT = [
     ("bf16", 8, 2, 64, [1, 1, 1], [300, 90, 1]),
     ("bf16", 128, 4, 300, [1, 1, 2], [4000, 1000, 20]),
     ("bf16", 128, 4, 100, [1, 2], [20000, 17000]),          # over 4096 candidates
+    ("bf16", 64, 1, 5000, [1, 2], [9000, 6000]),            # more kept blocks than LDS stages
+    ("f32", 32, 2, 4096, [1, 1], [8200, 3000]),             # exactly as many as it stages
+    ("bf16", 128, 4, 2000, [1], [6000]),                    # every candidate kept, over 1024
 ]
 
 
