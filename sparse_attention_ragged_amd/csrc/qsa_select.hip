@@ -28,7 +28,7 @@ namespace {
 
 constexpr int kSelThreads = 256;    // scoring kernel
 constexpr int kTopkThreads = 1024;  // selection kernel: sixteen wavefronts hide its LDS latency
-constexpr int kScoreRounds = 4;      // blocks per team in the scoring kernel
+constexpr int kScoreRounds = 8;      // blocks per team in the scoring kernel (loads in flight)
 
 template <int DT>
 __device__ __forceinline__ float dot16(const u32x4 &a, const u32x4 &b)
