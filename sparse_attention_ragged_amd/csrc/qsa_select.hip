@@ -13,8 +13,8 @@
 // a team of head_dim * elem / 16 lanes, one 16-byte chunk each, reduced with DPP and
 // lane shuffles; a workgroup covers consecutive blocks of one row. Selection runs one
 // workgroup per row over the row's scores held in LDS as order-preserving integer
-// keys: an MSB-first radix select (up to four 8-bit digit histograms with LDS atomics,
-// one histogram per wavefront; it stops once every key left in the chosen bin is
+// keys: an MSB-first radix select (up to three digit histograms of 11, 11 and 10 bits
+// with LDS atomics, two copies each; it stops once every key left in the chosen bin is
 // needed) finds the high bits of the k-th largest key and how many keys sharing them
 // are needed; then each thread takes a contiguous segment of candidates, counts its
 // keys above that bin and in it, and after one workgroup scan of those counts emits
@@ -117,17 +117,31 @@ __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t *s_
     return before + inc - v;
 }
 
+// The same, also giving the workgroup's total.
+template <int TH>
+__device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t *s_wave, uint32_t &total)
+{
+    const uint32_t before = block_exclusive_sum<TH>(v, s_wave);
+    total = 0u;
+#pragma unroll
+    for (int w = 0; w < TH / 64; ++w)
+        total += s_wave[w];
+    return before;
+}
+
 template <int CAP>
 __global__ __launch_bounds__(kTopkThreads) void select_topk_kernel(SelectParams p)
 {
     constexpr int TH = kTopkThreads;
     constexpr int NW = TH / 64;
+    constexpr int kBins = 2048;                               // 11-bit digits
+    static_assert(2 * TH == kBins, "each thread scans two bins");
     __shared__ uint32_t s_key[CAP];
-    // one histogram per wavefront during the radix select; afterwards the kept blocks
-    // in rank order (when they fit), so the outputs are written coalesced
-    constexpr int kStaged = NW * 256;
-    __shared__ uint32_t s_hist[NW][256];
-    __shared__ uint32_t s_bin[256];                           // the wavefronts' histograms summed
+    // two copies of the digit histogram (even and odd wavefronts) during the radix
+    // select; afterwards the kept blocks in rank order (when they fit), so the outputs
+    // are written coalesced
+    constexpr int kStaged = 2 * kBins;
+    __shared__ uint32_t s_hist[2][kBins];
     uint32_t *s_sel = &s_hist[0][0];
     __shared__ uint32_t s_wave[NW];
     __shared__ uint32_t s_digit[3];                           // chosen digit, keys still needed, keys in its bin
@@ -164,55 +178,41 @@ __global__ __launch_bounds__(kTopkThreads) void select_topk_kernel(SelectParams 
                     s_key[i] = order_key(v[u]);
             }
         }
+        // digits: bits 31..21, 20..10, 9..0
         uint32_t prefix = 0u, mask = 0u, remaining = (uint32_t)k;
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            for (int i = tid; i < NW * 256; i += TH)
+        for (int pass = 0; pass < 3; ++pass) {
+            const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+            const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+            for (int i = tid; i < 2 * kBins; i += TH)
                 (&s_hist[0][0])[i] = 0u;
             __syncthreads();
+            uint32_t *hist = s_hist[wave & 1];
 #pragma unroll 8
             for (int64_t i = tid; i < nv; i += TH) {
                 const uint32_t key = s_key[i];
                 if ((key & mask) == prefix)
-                    atomicAdd(&s_hist[wave][(key >> shift) & 255u], 1u);
+                    atomicAdd(&hist[(key >> shift) & dmask], 1u);
             }
             __syncthreads();
-            if (tid < 256) {
-                uint32_t h = 0u;
-#pragma unroll
-                for (int w = 0; w < NW; ++w)
-                    h += s_hist[w][tid];
-                s_bin[tid] = h;
-            }
-            __syncthreads();
-            if (tid < 64) {
-                // lane l holds bins 4l .. 4l+3; suffix sums from the top bin down
-                uint32_t h[4], local = 0u;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    h[e] = s_bin[4 * tid + e];
-                    local += h[e];
-                }
-                // inclusive suffix sum over lanes (lane l: sum of lanes l..63)
-                uint32_t suf = local;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const uint32_t v = (uint32_t)__shfl_down((int)suf, off);
-                    suf += tid + off < 64 ? v : 0u;
-                }
-                uint32_t sc = suf - local;                      // keys in bins above bin e
-#pragma unroll
-                for (int e = 3; e >= 0; --e) {
-                    if (sc < remaining && sc + h[e] >= remaining) {
-                        s_digit[0] = (uint32_t)(4 * tid + e);
-                        s_digit[1] = remaining - sc;
-                        s_digit[2] = h[e];
-                    }
-                    sc += h[e];
-                }
+            // thread t holds bins 2t and 2t + 1; keys in higher bins come from the scan
+            const uint32_t h0 = s_hist[0][2 * tid] + s_hist[1][2 * tid];
+            const uint32_t h1 = s_hist[0][2 * tid + 1] + s_hist[1][2 * tid + 1];
+            uint32_t total;
+            const uint32_t below = block_exclusive_sum<TH>(h0 + h1, s_wave, total);
+            const uint32_t above1 = total - below - h0 - h1;
+            const uint32_t above0 = above1 + h1;
+            if (above1 < remaining && above1 + h1 >= remaining) {
+                s_digit[0] = (uint32_t)(2 * tid + 1);
+                s_digit[1] = remaining - above1;
+                s_digit[2] = h1;
+            } else if (above0 < remaining && above0 + h0 >= remaining) {
+                s_digit[0] = (uint32_t)(2 * tid);
+                s_digit[1] = remaining - above0;
+                s_digit[2] = h0;
             }
             __syncthreads();
             prefix |= s_digit[0] << shift;
-            mask |= 255u << shift;
+            mask |= dmask << shift;
             remaining = s_digit[1];
             const bool all_of_bin = s_digit[2] == remaining;
             __syncthreads();
