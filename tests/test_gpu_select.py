@@ -95,6 +95,7 @@ EXACT = [
     ("bf16", 64, 1, 5000, [1, 2], [9000, 6000]),            # more kept blocks than LDS stages
     ("f32", 32, 2, 4096, [1, 1], [8200, 3000]),             # exactly as many as it stages
     ("bf16", 128, 4, 2000, [1], [6000]),                    # every candidate kept, over 1024
+    ("f32", 256, 2, 9, [2, 1], [300, 77]),                  # 1024-byte key rows: 64-lane teams
 ]
 
 
