@@ -30,14 +30,14 @@
  *     allocates, frees or synchronises, and reads no device data on the host.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).
  *   - Workspace: the size the matching *_workspace_size call reports, 16-byte
- *     aligned. Its last 256 bytes hold a work counter of the dynamic schedule that
- *     must be zero when a call starts and that every call leaves zero: zero-fill a
- *     workspace once before its first call. Calls that share a workspace must be
- *     ordered (one stream, or synchronised); calls on different workspaces may overlap.
+ *     aligned, contents undefined on entry (every byte a call reads there it has
+ *     written earlier in the same call). Calls that share a workspace must be ordered
+ *     (one stream, or synchronised); calls on different workspaces may overlap.
  *   - Arguments are checked on the host before anything is launched; a failed
- *     check returns a non-zero qsa_status and qsa_last_error() describes it
- *     ("Raises: Error: If the operand shapes disagree with the parameters" on the
- *     pages becomes a status code here).
+ *     check returns a non-zero qsa_status and qsa_last_error() describes it. (Where
+ *     the pages' ops raise an error for operand shapes that contradict their
+ *     parameters - "QSASparseAttentionRaggedPaged", Raises - this library returns
+ *     a status code instead.)
  *   - Row r of sequence b (input_row_offsets[b] <= r < input_row_offsets[b+1]) is
  *     at position cache_lengths[b] + (r - input_row_offsets[b]); the cache already
  *     holds positions 0 .. that position. Only block-sparse (causal clip) and latent
@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 4
+#define QSA_ABI_VERSION 5
 
 /* Element types. QSA_FP8_E4M3 is the OCP 8-bit E4M3 "fn" format (bias 7, max 448,
  * no infinity), scale-free as the block-sparse page states for its FP8 path. */
@@ -112,24 +112,13 @@ typedef struct {
     uint32_t reserved1;
 } qsa_ragged_q;
 
-/* Work schedule of the wavefront kernel (groups of 1, 2 or 4 query heads per kv head).
- * STATIC: one workgroup per (row, kv head, split); bitwise reproducible. DYNAMIC: each
- * (row, kv head) key list is cut into units of a few key batches and a persistent grid
- * takes the units from a counter in the workspace as workgroups free up; the units'
- * partials are merged by the split-K combine step. Results agree with STATIC to fp32
- * rounding but are not bitwise reproducible from call to call. AUTO is STATIC (the
- * faster of the two on the decode workloads measured). The matrix-core kernels always
- * run STATIC (DYNAMIC is refused there). */
-typedef enum { QSA_SCHEDULE_AUTO = 0, QSA_SCHEDULE_STATIC = 1, QSA_SCHEDULE_DYNAMIC = 2 } qsa_schedule;
-
 /* Launch knobs ("QSASparseAttentionRaggedPaged" execute Parameters: warps per CTA
- * and keys in flight). Pass NULL, or zeros, for the library's choice. Under the
- * dynamic schedule num_splits, waves and unroll are chosen by the library. */
+ * and keys in flight). Pass NULL, or zeros, for the library's choice. */
 typedef struct {
     int32_t num_splits;      /* split-K partitions of each row's key list; 0 = automatic */
     int32_t waves;           /* wavefronts per workgroup; 0 = automatic */
     int32_t unroll;          /* gathered keys a key team has in flight; 0 = automatic */
-    int32_t schedule;        /* qsa_schedule */
+    int32_t reserved;        /* must be 0 */
 } qsa_launch_options;
 
 /* ------------------------------------------------------------------------- */
@@ -231,7 +220,7 @@ qsa_status qsa_latent_sparse_attention(void *out, int32_t out_dtype, const qsa_r
  *   causal   0 (no mask) or 1 (causal)
  *   window   -1 for none, else >= 1 (the pages' local_window_size)
  * Supported: the same (dtype, group, head_dim) as qsa_sparse_attention; groups of
- * more than 16 are not built here. The dynamic schedule is refused.
+ * more than 16 are not built here.
  */
 qsa_status qsa_ragged_attention_workspace_size(const qsa_ragged_q *q, int64_t num_kv_heads, int32_t causal,
                                                int64_t window, const qsa_launch_options *opts,

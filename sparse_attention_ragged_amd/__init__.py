@@ -2,8 +2,9 @@
 
 Argument marshalling only: every step of the computation runs in the HIP kernels
 behind the C ABI declared in ``include/qsa.h``. PyTorch supplies device memory and
-the current stream. There is no fallback path: if the built library is missing the
-import fails, and the functions refuse CPU tensors.
+the current stream. There is no fallback path: the import builds the library from
+csrc/ when it is missing or out of date and fails if it cannot, and the functions
+refuse CPU tensors.
 
 Entry points (same names as the C ABI, without the ``qsa_`` prefix):
 
@@ -72,20 +73,21 @@ class _Ragged(ctypes.Structure):
                 ("reserved1", ctypes.c_uint32)]
 
 
-SCHEDULE_CODE = {"auto": 0, "static": 1, "dynamic": 2}
-
-
 class LaunchOptions(ctypes.Structure):
-    """Launch knobs: split-K partitions, wavefronts per workgroup, keys in flight (0 = auto)
-    and the work schedule (0 auto, 1 static, 2 dynamic)."""
+    """Launch knobs: split-K partitions, wavefronts per workgroup, keys in flight (0 = auto)."""
     _fields_ = [("num_splits", ctypes.c_int32), ("waves", ctypes.c_int32),
-                ("unroll", ctypes.c_int32), ("schedule", ctypes.c_int32)]
+                ("unroll", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError("libqsa.so is not built (%s); run sparse_attention_ragged_amd/build.py "
-                          "or __graft_entry__.build()" % LIB_PATH)
+    # libqsa.so is a build product (not kept in version control): build it from csrc/
+    # when it is missing or was built from other sources. Without hipcc that fails
+    # loudly; there is no other implementation to fall back to.
+    from . import build as _build
+    try:
+        _build.ensure_built()
+    except Exception as e:          # noqa: BLE001 - re-raised as the import failure it is
+        raise ImportError("libqsa.so could not be built from %s: %s" % (_build.CSRC, e)) from e
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     pc, pr, po = ctypes.POINTER(_Cache), ctypes.POINTER(_Ragged), ctypes.POINTER(LaunchOptions)
@@ -189,9 +191,10 @@ def _opts(options):
         return None
     if isinstance(options, LaunchOptions):
         return ctypes.byref(options)
-    sched = options.get("schedule", 0)
-    sched = SCHEDULE_CODE[sched] if isinstance(sched, str) else int(sched)
-    o = LaunchOptions(options.get("num_splits", 0), options.get("waves", 0), options.get("unroll", 0), sched)
+    unknown = set(options) - {"num_splits", "waves", "unroll"}
+    if unknown:
+        raise ValueError("unknown launch options: %s" % ", ".join(sorted(unknown)))
+    o = LaunchOptions(options.get("num_splits", 0), options.get("waves", 0), options.get("unroll", 0), 0)
     return ctypes.byref(o)
 
 
@@ -205,9 +208,7 @@ def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
     if nbytes == 0:
         return None, 0
     if workspace is None:
-        # zero-filled: the dynamic schedule's work counter must start at zero (every
-        # call leaves it zero, so a workspace passed back in needs no refill)
-        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
     elif workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError("workspace too small: %d bytes needed" % nbytes)
     return workspace, workspace.numel() * workspace.element_size()

@@ -45,14 +45,9 @@ void fill_common(GatherParams &p, void *out, int32_t out_dtype, const qsa_ragged
     p.split_keys = plan.split_keys;
     p.split_row0 = plan.split_row0;
     p.head_block = plan.head_block;
-    if (plan.num_splits > 1 || plan.schedule == SCHED_DYNAMIC) {
+    if (plan.num_splits > 1) {
         p.ws_acc = static_cast<float *>(ws);
         p.ws_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + plan.ws_ml_offset);
-    }
-    if (plan.schedule == SCHED_DYNAMIC) {
-        p.sched_counter = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + plan.ws_ctr_offset);
-        p.sched_bpu = plan.sched_bpu;
-        p.sched_grid = plan.sched_grid;
     }
 }
 
@@ -63,16 +58,13 @@ qsa_status run(const GatherParams &p, const Plan &plan, void *stream)
     int err = 0;
     if (t_ev_start && t_ev_stop)
         err = record_event(t_ev_start, stream);
-    const bool dyn = plan.schedule == SCHED_DYNAMIC;
     if (!err)
-        err = dyn                          ? launch_gather_valu_dyn(p, stream)
-              : plan.path == PATH_MFMA_WIDE ? launch_gather_mfma_wide(p, stream)
-              : plan.path == PATH_MFMA      ? launch_gather_mfma(p, stream)
-                                            : launch_gather_valu(p, stream);
+        err = plan.path == PATH_MFMA_WIDE ? launch_gather_mfma_wide(p, stream)
+              : plan.path == PATH_MFMA    ? launch_gather_mfma(p, stream)
+                                          : launch_gather_valu(p, stream);
     if (!err && t_ev_start && t_ev_stop)
         err = record_event(t_ev_stop, stream);
-    // the combine step also returns the dynamic schedule's counter to zero
-    if (!err && (plan.num_splits > 1 || dyn))
+    if (!err && plan.num_splits > 1)
         err = launch_splitk_combine(p, stream);
     if (err)
         return fail(QSA_ERR_HIP, "HIP launch failed: %s", hip_error_text(err));
@@ -389,7 +381,7 @@ qsa_status qsa_ragged_attention(void *out, int32_t out_dtype, const qsa_ragged_q
     p.window = window > 0 ? window : 0;
     // matrix-core groups without a split: workgroups of consecutive rows share key tiles
     // (unless a launch option asks for a wavefront count, which only the per-row kernel takes)
-    if (plan.path == PATH_MFMA && plan.num_splits == 1 && plan.schedule == SCHED_STATIC &&
+    if (plan.path == PATH_MFMA && plan.num_splits == 1 &&
         (!opts || opts->waves == 0) && mfma_flash_supported(q->dtype, p.group, p.head_dim)) {
         if (q->total_q == 0)
             return QSA_OK;

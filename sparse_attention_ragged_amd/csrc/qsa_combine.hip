@@ -8,8 +8,6 @@
 //   out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,   M = max_s m_s,
 // and a (row, head) that saw no key anywhere (l = 0 everywhere) is written as zeros.
 // A per-head sink logit (latent attention) joins the denominator here, once.
-// After a dynamically scheduled gather this kernel also returns the work counter to
-// zero (the gather has finished: it runs earlier on the same stream).
 #include "qsa_device.hpp"
 
 namespace qsa {
@@ -27,8 +25,6 @@ __global__ void __launch_bounds__(256) splitk_combine_kernel(GatherParams p)
     const int64_t rel = (int64_t)blockIdx.x * per_block + threadIdx.x / tpr;
     const int64_t rh = p.split_row0 * p.num_q_heads + rel;
     const int d0 = (threadIdx.x % tpr) * 4;
-    if (p.sched_counter && blockIdx.x == 0 && threadIdx.x == 0)
-        *p.sched_counter = 0u;
     if (rel >= RH || threadIdx.x / tpr >= per_block)
         return;
     const int S = p.num_splits;

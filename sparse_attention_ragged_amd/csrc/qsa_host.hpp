@@ -82,16 +82,8 @@ struct GatherParams {
     int64_t split_keys;              // keys per split (in key-list units)
     int64_t split_row0;              // rows before it run unsplit (head-split kernel's tail plan)
     int32_t head_block;              // wavefront kernel: kv heads one workgroup covers
-    float *ws_acc;                   // [S, total_q, Hq, D] when num_splits > 1 or scheduled
+    float *ws_acc;                   // [S, total_q, Hq, D] when num_splits > 1
     float *ws_ml;                    // [S, total_q, Hq, 2]
-    uint32_t *sched_counter;         // dynamic schedule: units handed out (zero at launch)
-    int32_t sched_bpu;               // dynamic schedule: key batches per unit
-    int32_t sched_grid;              // dynamic schedule: persistent workgroups
-};
-
-enum Schedule : int32_t {
-    SCHED_STATIC = 0,     // one workgroup per (row, kv head, split)
-    SCHED_DYNAMIC = 1,    // persistent workgroups take key-range units from a counter
 };
 
 enum GatherPath : int32_t {
@@ -109,12 +101,8 @@ struct Plan {
     int64_t split_keys;
     int64_t split_row0;     // rows before it run unsplit; the rest num_splits ways (0: all rows)
     int32_t head_block;     // wavefront kernel: kv heads per workgroup (1 for other paths)
-    int32_t schedule;       // Schedule
-    int32_t sched_bpu;      // SCHED_DYNAMIC: key batches per unit
-    int32_t sched_grid;     // SCHED_DYNAMIC: persistent workgroups
     size_t ws_bytes;
     size_t ws_ml_offset;
-    size_t ws_ctr_offset;   // SCHED_DYNAMIC: the unit counter
 };
 
 // Team layout of the wavefront kernel, shared by the kernel and the planner: a key's
@@ -129,13 +117,6 @@ constexpr int valu_team_lanes(int elem_bytes, int head_dim)
     return head_dim * elem_bytes / (16 * valu_chunks_per_lane(elem_bytes, head_dim));
 }
 
-// Dynamically scheduled wavefront kernel: one workgroup per CU (two streams of 4 and
-// 3 streaming wavefronts plus a control wavefront); a unit is kDynBatchesPerUnit key
-// batches of the 4-wavefront stream (4 x teams-per-wavefront x 2 keys each).
-constexpr int kDynUnitWaves = 4;
-constexpr int kDynBatchesPerUnit = 4;
-constexpr int kDynWorkgroups = 256;   // one per CU
-
 // Validation + planning (qsa_plan.cpp). They never touch the device.
 qsa_status check_cache(const qsa_paged_cache *c, const char *what, int64_t planes);
 qsa_status check_q(const qsa_ragged_q *q, const qsa_paged_cache *c, bool same_heads_as_cache);
@@ -146,7 +127,6 @@ CacheAddr cache_addr(const qsa_paged_cache *c, uint32_t layer);
 
 // Launchers (qsa_*.hip). Return a hipError_t value (0 = success).
 int launch_gather_valu(const GatherParams &p, void *stream);
-int launch_gather_valu_dyn(const GatherParams &p, void *stream);
 int launch_gather_mfma(const GatherParams &p, void *stream);
 int launch_gather_mfma_wide(const GatherParams &p, void *stream);
 int launch_splitk_combine(const GatherParams &p, void *stream);

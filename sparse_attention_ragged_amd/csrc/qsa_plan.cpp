@@ -147,65 +147,12 @@ qsa_status plan_gather(const qsa_ragged_q *q, int64_t num_kv_heads, int32_t dtyp
         return fail(QSA_ERR_UNSUPPORTED, "waves must be in [0, 8] (0 = automatic)");
     if (o.unroll < 0 || o.unroll > 8)
         return fail(QSA_ERR_UNSUPPORTED, "unroll must be in [0, 8]");
-    if (o.schedule < QSA_SCHEDULE_AUTO || o.schedule > QSA_SCHEDULE_DYNAMIC)
-        return fail(QSA_ERR_UNSUPPORTED, "schedule must be QSA_SCHEDULE_AUTO, _STATIC or _DYNAMIC");
+    if (o.reserved != 0)
+        return fail(QSA_ERR_UNSUPPORTED, "qsa_launch_options.reserved must be 0");
     plan->waves = o.waves ? o.waves : 4;
     plan->unroll = o.unroll ? o.unroll : 4;
     plan->key_capacity = key_capacity;
-    plan->schedule = SCHED_STATIC;
-    plan->sched_bpu = 0;
-    plan->sched_grid = 0;
-    plan->ws_ctr_offset = 0;
     const int64_t cap = key_capacity > 0 ? key_capacity : 1;
-
-    if (list_kind == KEYS_DENSE && o.schedule == QSA_SCHEDULE_DYNAMIC) {
-        return fail(QSA_ERR_UNSUPPORTED, "the dynamic schedule does not take dense attention");
-    }
-
-    // Dynamic schedule (wavefront kernel, one kv head per workgroup), on request only:
-    // every (row, kv head) list is cut into units of a few key batches and a persistent
-    // grid takes them from a counter. It evens out the uneven finish of static shares,
-    // but measured slower than the static schedule on the decode workloads (it keeps
-    // seven streaming wavefronts per CU instead of eight and merges per unit), so the
-    // automatic choice is the static schedule.
-    if (plan->path == PATH_VALU && o.schedule == QSA_SCHEDULE_DYNAMIC && list_kind != KEYS_DENSE) {
-        const int eb = dtype == QSA_F32 ? 4 : dtype == QSA_BF16 ? 2 : 1;
-        const int64_t per_batch = (int64_t)kDynUnitWaves * (64 / valu_team_lanes(eb, Dh)) * 2;
-        int64_t bpu = kDynBatchesPerUnit;
-        int64_t parts = ceil_div(cap, bpu * per_batch);
-        if (parts > kMaxSplits) {
-            bpu = ceil_div(cap, kMaxSplits * per_batch);
-            parts = ceil_div(cap, bpu * per_batch);
-        }
-        // the shortest unit that still covers the capacity in `parts` units
-        bpu = ceil_div(ceil_div(cap, parts), per_batch);
-        if (bpu < 3)
-            bpu = 3;
-        const int64_t units = q->total_q * num_kv_heads * parts;
-        if (units >= ((int64_t)1 << 31))
-            return fail(QSA_ERR_UNSUPPORTED, "dynamic schedule: %lld units out of range", (long long)units);
-        if (units > 0) {                 // (an empty batch has nothing to schedule)
-            plan->schedule = SCHED_DYNAMIC;
-            plan->head_block = 1;
-            plan->waves = 7;
-            plan->unroll = 2;
-            plan->num_splits = (int32_t)parts;
-            plan->split_keys = bpu * per_batch;
-            plan->sched_bpu = (int32_t)bpu;
-            plan->sched_grid = (int32_t)(units < kDynWorkgroups ? units : kDynWorkgroups);
-            size_t rows_heads = (size_t)q->total_q * (size_t)q->num_q_heads;
-            size_t acc = (size_t)parts * rows_heads * (size_t)q->head_dim * sizeof(float);
-            acc = (acc + 255) & ~(size_t)255;
-            size_t ml = (size_t)parts * rows_heads * 2 * sizeof(float);
-            ml = (ml + 255) & ~(size_t)255;
-            plan->ws_ml_offset = acc;
-            plan->ws_ctr_offset = acc + ml;
-            plan->ws_bytes = acc + ml + 256;
-            return QSA_OK;
-        }
-    } else if (o.schedule == QSA_SCHEDULE_DYNAMIC) {
-        return fail(QSA_ERR_UNSUPPORTED, "the dynamic schedule runs the wavefront kernel (groups of 1, 2, 4) only");
-    }
 
     // wavefront kernel: when every kv head reads the same keys and there are too few
     // (row, kv head) items to fill the device without splitting, one workgroup covers a

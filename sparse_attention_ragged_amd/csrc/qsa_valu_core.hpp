@@ -1,9 +1,8 @@
 // Per-team core of the wavefront gather kernels (groups of 1, 2 or 4 query heads per
 // kv head): the register layout of a key's K/V rows over a team of lanes, the scoring
 // of a batch of U keys per team against the q rows, the online-softmax fold and the
-// merge of teams. The statically scheduled kernel (one workgroup per (row, kv head,
-// split)) and the dynamically scheduled one (persistent workgroups taking key ranges
-// from a counter) both run it.
+// merge of teams, run by the wavefront gather kernel (one workgroup per (row, kv
+// head, split)).
 //
 //  * Teams: a team of TL lanes owns one (key, kv head) at a time; each lane holds CPL
 //    16-byte chunks of the K row and of the V row (chunk c of lane l is chunk c*TL + l
@@ -206,17 +205,12 @@ struct ValuCore {
         }
     }
 
-    // merge with the team OFF lanes away (butterfly step). kSerial: one head at a time
-    // behind scheduling fences, so that the permute copies of only one head are live
-    // (for merges in the middle of a stream, where the next batches' loads hold
-    // registers).
-    template <int OFF, bool kSerial = false>
+    // merge with the team OFF lanes away (butterfly step)
+    template <int OFF>
     __device__ __forceinline__ void merge_pair()
     {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            if constexpr (kSerial)
-                __builtin_amdgcn_sched_barrier(0);
             float ma, mb, la, lb;
             xor_pair<OFF>(m[h], ma, mb);
             xor_pair<OFF>(l[h], la, lb);
@@ -234,51 +228,15 @@ struct ValuCore {
         }
     }
 
-    // Lane-wise op over the teams of a wavefront (teams of one kv head, HB = 1): DPP
-    // rotations within a 16-lane row (fused into the op), LDS-path permutes across rows.
-    template <typename Op>
-    __device__ __forceinline__ static float across_teams(float x, Op op)
-    {
-        if constexpr (TL <= 4)
-            x = op(x, dpp_f<0x124>(x));         // row_ror:4
-        if constexpr (TL <= 8)
-            x = op(x, dpp_f<0x128>(x));         // row_ror:8
-        if constexpr (TL <= 16)
-            x = op(x, __shfl_xor(x, 16));
-        return op(x, __shfl_xor(x, 32));
-    }
-
-    // Merge of all teams of a wavefront (one kv head per wavefront) for a flush in the
-    // middle of a stream: the wavefront's largest reference per head first, one
-    // rescale, then plain sums over the teams. About a third of the vector-ALU work of
-    // the pairwise butterfly, whose every step rescales both halves; afterwards every
-    // team holds the merged state.
-    __device__ __forceinline__ void merge_teams_lean()
-    {
-        auto fmax_ = [](float a, float b) { return fmaxf(a, b); };
-        auto add_ = [](float a, float b) { return a + b; };
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float mw = across_teams(m[h], fmax_);
-            const float c = __builtin_amdgcn_exp2f(m[h] - mw);
-            l[h] = across_teams(l[h] * c, add_);
-#pragma unroll
-            for (int e = 0; e < EPL; ++e)
-                acc[h][e] = across_teams(acc[h][e] * c, add_);
-            m[h] = mw;
-        }
-    }
-
     // merge the teams of a wavefront whose lanes are `span` or more apart (teams of the
     // same kv head sit span lanes apart): afterwards every such team holds the
     // wavefront's state for its head
-    template <bool kSerial = false>
     __device__ __forceinline__ void merge_teams(int span)
     {
-        if constexpr (TL <= 4) if (4 >= span) merge_pair<4, kSerial>();
-        if constexpr (TL <= 8) if (8 >= span) merge_pair<8, kSerial>();
-        if constexpr (TL <= 16) if (16 >= span) merge_pair<16, kSerial>();
-        if constexpr (TL <= 32) if (32 >= span) merge_pair<32, kSerial>();
+        if constexpr (TL <= 4) if (4 >= span) merge_pair<4>();
+        if constexpr (TL <= 8) if (8 >= span) merge_pair<8>();
+        if constexpr (TL <= 16) if (16 >= span) merge_pair<16>();
+        if constexpr (TL <= 32) if (32 >= span) merge_pair<32>();
     }
 };
 

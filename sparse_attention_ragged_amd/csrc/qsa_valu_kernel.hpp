@@ -1,0 +1,317 @@
+// Gather-attention kernel on wavefront dot products (groups of 1, 2 or 4 query
+// heads per kv head). Included by one translation unit per element type
+// (qsa_valu_f32.hip, qsa_valu_bf16.hip, qsa_valu_e4m3.hip), so the instances build in parallel.
+//
+// One workgroup owns one (query row, kv head, split) and walks that split of the
+// row's key list ("QSASparseAttentionRaggedPaged": token_indices up to counts;
+// "Struct_msa_attention_ragged_paged": the positions of the listed blocks up to the
+// row's position; "latent_sparse_attention_ragged_paged": window positions, then
+// listed compressed entries). The per-team scoring, softmax fold and team merge are
+// the shared core of qsa_valu_core.hpp.
+//
+//  * Head blocks: when all kv heads read the same keys (token-index and latent
+//    lists), a workgroup covers a block of HB kv heads and the teams of a wavefront
+//    are HB heads x (64/TL/HB) key slots. At HB = 8 (bf16, head_dim 128, 8 kv heads) a
+//    wavefront reads a key's whole K block and V block (all heads, contiguous in the
+//    page) with one request each, and the key's address is computed once per
+//    wavefront. Key slots take keys j0 + b*NK*U + u*NK + slot (batch b, u < U, NK slots
+//    per workgroup).
+//  * Address pipeline (the pages' `unroll` keys in flight, and more): while batch b
+//    is folded into the softmax state, the K/V rows of batch b+1 are in flight, the
+//    page-table entries of batch b+2 and the list entries of batch b+3. Every stage
+//    issues one load per key on every path (dummies for absent keys), so the compiler
+//    waits for exactly the oldest batch. There is no staging phase and no barrier
+//    before the first K/V load: a workgroup reaches full speed after three memory
+//    latencies.
+//  * Merge: teams of a wavefront merge with lane shuffles, wavefronts through LDS;
+//    the result is the normalised output row (one split) or an (m, l, acc) partial
+//    for the split-K combine kernel.
+#pragma once
+
+#include <atomic>
+#include <type_traits>
+
+#include "qsa_valu_core.hpp"
+
+namespace qsa {
+
+namespace {
+
+constexpr int kMaxWaves = 8;
+
+template <int DT, int D, int G, int U, int LIST>
+__global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParams p)
+{
+    using Core = ValuCore<DT, D, G, U>;
+    constexpr int EB = Core::EB;
+    constexpr int EPC = Core::EPC;
+    constexpr int CPL = Core::CPL;
+    constexpr int TL = Core::TL;
+    constexpr int TPW = Core::TPW;
+    extern __shared__ __attribute__((aligned(16))) float smem[];   // [NW][HB*G][2], then [NW][HB*G][D]
+
+    const int S = p.num_splits;
+    const int HB = p.head_block;                 // kv heads of this workgroup, one team each
+    uint32_t bid = blockIdx.x;                   // grid < 2^31 (checked by the launcher)
+    const uint32_t nhb = (uint32_t)(p.num_kv_heads / HB);
+    const int gb = (int)(bid % nhb);
+    bid /= nhb;
+    const int s = (int)(bid % (uint32_t)S);
+    const int64_t r = bid / (uint32_t)S;
+
+    const int tid = threadIdx.x;
+    const int nthreads = blockDim.x;
+    const int ln = tid % TL;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int NW = nthreads >> 6;
+    const int tw = lane / TL;                    // team within the wavefront
+    const int hh = tw % HB;                      // its kv head within the block
+    const int ks = tw / HB;                      // its key slot within the wavefront
+    const int KPW = TPW / HB;                    // key slots per wavefront
+    const int g = gb * HB + hh;
+    const int NK = NW * KPW;                     // key slots per workgroup
+
+    // prologue: list length and the q rows go out together
+    int64_t n = LIST == KEYS_DENSE ? 0 : key_list_length(p, r);
+    const char *qbase = static_cast<const char *>(p.q) + ((r * p.num_q_heads + (int64_t)g * G) * D) * EB;
+    typename Core::Q q;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            q.raw[h][c] = ldg16(qbase + ((int64_t)h * D + Core::chunk_elem(c, ln)) * EB);
+    int64_t pos = 0;
+    const int b = find_seq_pos_wave(p.row_off,
+                                    LIST == KEYS_TOKEN_INDICES || LIST == KEYS_DENSE ? nullptr : p.cache_lengths,
+                                    p.batch, (uint32_t)r, pos);
+    if constexpr (LIST == KEYS_DENSE)
+        n = dense_key_range(p, r, b, pos);     // pos: row index of the row's first key
+    const int64_t j0 = (int64_t)s * p.split_keys;
+    const int64_t jend = j0 + p.split_keys;
+    const int64_t j1 = n < jend ? n : jend;
+    const int64_t per_batch = (int64_t)NK * U;
+    const int nb = j1 > j0 ? (int)((j1 - j0 + per_batch - 1) / per_batch) : 0;
+    const int64_t vdelta = LIST == KEYS_LATENT  ? 0
+                           : LIST == KEYS_DENSE ? static_cast<const char *>(p.dense_v) - static_cast<const char *>(p.dense_k)
+                                                : (int64_t)p.kv.plane_stride_b;
+    const char *dummy = qbase;                   // a readable row for absent keys
+
+    Core::widen_q(q);
+    Core st;
+    st.reset();
+
+    // ---- pipeline stages (each issues exactly one load per key on every path)
+    struct Entries { int32_t raw[U]; };
+    struct Pages { KeyPos k[U]; int32_t slot[U]; uint32_t page[U]; };
+    using Rows = typename Core::Rows;
+
+    auto key_index = [&](int batch, int u) -> int64_t {
+        return j0 + batch * per_batch + u * NK + wave * KPW + ks;
+    };
+    auto load_entries = [&](int batch, Entries &E) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t jj = key_index(batch, u);
+            if constexpr (LIST == KEYS_DENSE)
+                E.raw[u] = 0;                      // dense: the key is its index, nothing to load
+            else
+                E.raw[u] = *entry_ptr<LIST>(p, r, g, jj, jj < j1);
+        }
+    };
+    auto load_pages = [&](int batch, const Entries &E, Pages &P) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t jj = key_index(batch, u);
+            P.k[u] = key_pos<LIST>(p, pos, jj, E.raw[u], jj < j1);
+            if constexpr (LIST == KEYS_DENSE) {
+                P.page[u] = 0;                     // dense: no page table
+                P.slot[u] = 0;
+            } else {
+                P.page[u] = *page_entry_ptr<LIST>(p, b, P.k[u], P.slot[u]);
+            }
+        }
+    };
+    auto load_rows = [&](const Pages &P, Rows &R) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            bool ok;
+            const char *a = row_address<EB, LIST>(p, P.k[u], P.page[u], P.slot[u], g, dummy, ok);
+            R.ok[u] = ok;
+            const char *base = ok ? a : dummy;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                R.k[u][c] = ldg16(base + (int64_t)Core::chunk_elem(c, ln) * EB);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                R.v[u][c] = ldg16((ok ? a + vdelta : dummy) + (int64_t)Core::chunk_elem(c, ln) * EB);
+        }
+    };
+    auto consume = [&](const Rows &R) { st.consume(R, q, p.scale_log2); };
+
+    // ---- the pipeline: iteration i issues entries(i+2), pages(i+1), rows(i) and
+    // folds rows(i-1). Register sets alternate between even and odd iterations.
+    if (nb > 0) {
+        Entries E0, E1;
+        Pages P0, P1;
+        Rows R0, R1;
+        load_entries(0, E0);
+        load_entries(1, E1);
+        load_pages(0, E0, P0);
+        // iterations 0 and 1 are peeled so that the loop is entered with the same
+        // loads in flight as at its back edge
+        load_entries(2, E0);
+        load_pages(1, E1, P1);
+        load_rows(P0, R0);
+        load_entries(3, E1);
+        load_pages(2, E0, P0);
+        load_rows(P1, R1);
+        consume(R0);
+        for (int i = 2; i <= nb; i += 2) {
+            load_entries(i + 2, E0);
+            load_pages(i + 1, E1, P1);
+            load_rows(P0, R0);
+            consume(R1);
+            if (i + 1 > nb)
+                break;
+            load_entries(i + 3, E1);
+            load_pages(i + 2, E0, P0);
+            load_rows(P1, R1);
+            consume(R0);
+        }
+    }
+
+    // merge the key slots of this wavefront (teams of the same kv head sit TL*HB
+    // lanes apart)
+    st.merge_teams(TL * HB);
+
+    // merge the wavefronts through LDS: the key-slot-0 team of each kv head writes it
+    const int HG = HB * G;                       // q heads of the workgroup
+    float *s_ml = smem;                          // [NW][HG][2]
+    float *s_acc = smem + ((NW * HG * 2 + 3) & ~3);   // [NW][HG][D], 16-byte aligned
+    if (ks == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const int hq = hh * G + h;
+            if (ln == 0) {
+                s_ml[(wave * HG + hq) * 2] = st.m[h];
+                s_ml[(wave * HG + hq) * 2 + 1] = st.l[h];
+            }
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+#pragma unroll
+                for (int e = 0; e < EPC; e += 4)
+                    *reinterpret_cast<float4 *>(&s_acc[(wave * HG + hq) * D + Core::chunk_elem(c, ln) + e]) =
+                        make_float4(st.acc[h][c * EPC + e], st.acc[h][c * EPC + e + 1], st.acc[h][c * EPC + e + 2],
+                                    st.acc[h][c * EPC + e + 3]);
+        }
+    }
+    // (the loads of the batches past the end that the pipeline issued stay in flight)
+    lds_barrier();
+    // each thread finishes two adjacent outputs
+    for (int idx = tid; idx < HG * D / 2; idx += nthreads) {
+        const int hq = (2 * idx) / D;
+        const int d = 2 * idx - hq * D;
+        float M = kNoKey;
+        for (int w = 0; w < NW; ++w)
+            M = fmaxf(M, s_ml[(w * HG + hq) * 2]);
+        float L = 0.f, A0 = 0.f, A1 = 0.f;
+        for (int w = 0; w < NW; ++w) {
+            const float c = __builtin_amdgcn_exp2f(s_ml[(w * HG + hq) * 2] - M);
+            const float2 a = *reinterpret_cast<const float2 *>(&s_acc[(w * HG + hq) * D + d]);
+            L += c * s_ml[(w * HG + hq) * 2 + 1];
+            A0 += c * a.x;
+            A1 += c * a.y;
+        }
+        const int64_t head = (int64_t)gb * HG + hq;
+        const int64_t rh = r * p.num_q_heads + head;
+        if (S == 1) {
+            const float f = final_factor(p, head, M, L);
+            store_out2(p.out, p.out_dtype, rh * D + d, A0 * f, A1 * f);
+        } else {
+            const int64_t srh = (int64_t)s * p.total_q * p.num_q_heads + rh;
+            *reinterpret_cast<float2 *>(&p.ws_acc[srh * D + d]) = make_float2(A0, A1);
+            if (d == 0) {
+                p.ws_ml[srh * 2] = M;
+                p.ws_ml[srh * 2 + 1] = L;
+            }
+        }
+    }
+}
+
+template <int DT, int D, int G, int U, int LIST>
+int launch_valu(const GatherParams &p, void *stream)
+{
+    const int64_t grid = p.total_q * (int64_t)(p.num_kv_heads / p.head_block) * p.num_splits;
+    if (grid <= 0)
+        return 0;
+    if (grid > 0x7fffffff)
+        return (int)hipErrorInvalidConfiguration;
+    // LDS of the cross-wavefront merge: (reference, sum) and D partial outputs per q head
+    const size_t hg = (size_t)p.waves * p.head_block * G;
+    const size_t lds = (((2 * hg + 3) & ~(size_t)3) + hg * D) * sizeof(float);
+    // allow more than the default dynamic LDS, once per device
+    static std::atomic<uint64_t> raised{0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        dev = 63;
+    if (!(raised.load() >> dev & 1u)) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gather_valu_kernel<DT, D, G, U, LIST>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess)
+            return (int)e;
+        raised.fetch_or(uint64_t(1) << dev);
+    }
+    hipLaunchKernelGGL((gather_valu_kernel<DT, D, G, U, LIST>), dim3((unsigned)grid), dim3(64 * p.waves),
+                       lds, static_cast<hipStream_t>(stream), p);
+    return (int)hipGetLastError();
+}
+
+// Two keys per team per batch: with two 16-byte chunks per lane that keeps as many
+// bytes in flight as four one-chunk keys, and the register sets of both batches stay
+// within the 256 VGPRs a wavefront has at two wavefronts per SIMD. (`unroll` is
+// accepted for compatibility of launch options and does not change the kernel.)
+template <int DT, int D, int G, int LIST>
+int launch_valu_u(const GatherParams &p, void *stream)
+{
+    return launch_valu<DT, D, G, 2, LIST>(p, stream);
+}
+
+template <int DT, int D, int LIST>
+int launch_valu_g(const GatherParams &p, void *stream)
+{
+    switch (p.group) {
+    case 1: return launch_valu_u<DT, D, 1, LIST>(p, stream);
+    case 2: return launch_valu_u<DT, D, 2, LIST>(p, stream);
+    case 4: return launch_valu_u<DT, D, 4, LIST>(p, stream);
+    default: return (int)hipErrorInvalidValue;
+    }
+}
+
+template <int DT, int LIST>
+int launch_valu_d(const GatherParams &p, void *stream)
+{
+    switch (p.head_dim) {
+    case 64: return launch_valu_g<DT, 64, LIST>(p, stream);
+    case 128: return launch_valu_g<DT, 128, LIST>(p, stream);
+    case 256: return launch_valu_g<DT, 256, LIST>(p, stream);
+    default: return (int)hipErrorInvalidValue;
+    }
+}
+
+// every list kind of one element type
+template <int DT>
+int launch_valu_lists(const GatherParams &p, void *stream)
+{
+    switch (p.list_kind) {
+    case KEYS_TOKEN_INDICES: return launch_valu_d<DT, KEYS_TOKEN_INDICES>(p, stream);
+    case KEYS_BLOCKS: return launch_valu_d<DT, KEYS_BLOCKS>(p, stream);
+    case KEYS_LATENT: return launch_valu_d<DT, KEYS_LATENT>(p, stream);
+    case KEYS_DENSE: return launch_valu_d<DT, KEYS_DENSE>(p, stream);
+    default: return (int)hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+}  // namespace qsa

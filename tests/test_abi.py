@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(qsa):
 
 
 def test_abi_version_and_struct_sizes(qsa):
-    assert qsa.lib.qsa_abi_version() == 4
+    assert qsa.lib.qsa_abi_version() == 5
     assert qsa.lib.qsa_struct_size(0) == ctypes.sizeof(qsa._Cache) == 104
     assert qsa.lib.qsa_struct_size(1) == ctypes.sizeof(qsa._Ragged) == 64
     assert qsa.lib.qsa_struct_size(2) == ctypes.sizeof(qsa.LaunchOptions) == 16
@@ -116,43 +116,8 @@ def test_workspace_checks(qsa):
     assert n.value == 0
 
 
-def test_dynamic_schedule_workspace(qsa):
-    """The dynamic schedule's workspace: per-unit partials (units of whole key batches,
-    at least three batches), then a 256-byte counter block at the end."""
-    q, kv = ragged(), cache()
-    n = ctypes.c_size_t(0)
-    dyn = qsa.LaunchOptions(0, 0, 0, 2)
-    assert qsa.lib.qsa_sparse_attention_workspace_size(ctypes.byref(q), ctypes.byref(kv), 64,
-                                                       ctypes.byref(dyn), ctypes.byref(n)) == 0
-    # bf16 head_dim 128: 8-lane teams, 8 per wavefront, units of 4 batches of a
-    # 4-wavefront stream, 2 keys a team -> 256 keys; W 64 fits one unit: 3 rows x 8 heads
-    acc = 1 * 3 * 8 * 128 * 4
-    ml = 1 * 3 * 8 * 2 * 4
-    assert n.value == acc + ((ml + 255) // 256) * 256 + 256
-    assert call_qsa(qsa, opts=dyn, W=64, ws=P, wsb=16) == 5 and "workspace" in msg(qsa)
-    # W 2048 -> 2048 / 256 = 8 units per (row, kv head)
-    assert qsa.lib.qsa_sparse_attention_workspace_size(ctypes.byref(q), ctypes.byref(kv), 2048,
-                                                       ctypes.byref(dyn), ctypes.byref(n)) == 0
-    acc = 8 * 3 * 8 * 128 * 4
-    ml = 8 * 3 * 8 * 2 * 4
-    assert n.value == acc + ((ml + 255) // 256) * 256 + 256
-    # automatic: 3 rows x 2 kv heads x 5 units is too few units for 256 workgroups -> static
-    sizes = []
-    for o in (qsa.LaunchOptions(0, 0, 0, 0), qsa.LaunchOptions(0, 0, 0, 1)):
-        assert qsa.lib.qsa_sparse_attention_workspace_size(ctypes.byref(q), ctypes.byref(kv), 2048,
-                                                           ctypes.byref(o), ctypes.byref(n)) == 0
-        sizes.append(n.value)
-    assert sizes[0] == sizes[1]
-
-
-def test_dynamic_schedule_refused_on_matrix_cores(qsa):
-    q, kv = ragged(num_q_heads=16), cache()          # group 8: matrix-core kernel
-    assert call_qsa(qsa, q=q, kv=kv, opts=qsa.LaunchOptions(0, 0, 0, 2)) == 4, msg(qsa)
-    assert "dynamic" in msg(qsa)
-
-
 @pytest.mark.parametrize("opts", [(65, 0, 0, 0), (0, 9, 0, 0), (0, 16, 0, 0), (0, 0, 9, 0), (-1, 0, 0, 0),
-                                  (0, 0, 0, 3), (0, 0, 0, -1)])
+                                  (0, 0, 0, 2), (0, 0, 0, 1), (0, 0, 0, -1)])
 def test_bad_launch_options(qsa, opts):
     assert call_qsa(qsa, opts=qsa.LaunchOptions(*opts)) == 4, msg(qsa)
 
@@ -176,7 +141,7 @@ def test_ragged_attention_checks(qsa):
     assert call(k=0) == 1 and call(v=0) == 1 and call(out=0) == 1
     assert call(k=P + 4) == 2                           # 16-byte alignment
     assert call(scale=float("nan")) == 2
-    assert call(opts=qsa.LaunchOptions(0, 0, 0, 2)) == 4 and "dynamic" in msg(qsa)
+    assert call(opts=qsa.LaunchOptions(0, 0, 0, 2)) == 4 and "reserved" in msg(qsa)
     n = ctypes.c_size_t(7)
     assert qsa.lib.qsa_ragged_attention_workspace_size(ctypes.byref(ragged()), 2, 1, -1, None,
                                                        ctypes.byref(n)) == 0

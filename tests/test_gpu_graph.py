@@ -1,6 +1,6 @@
 """The C-ABI calls inside a captured HIP graph (torch.cuda.CUDAGraph over the library's
-launches on the capture stream): the library allocates nothing, records no memset and
-resets the dynamic schedule's counter with a kernel, so a captured call can be replayed.
+launches on the capture stream): the library allocates nothing and records no memset,
+so a captured call can be replayed.
 Each graph is replayed several times with eager work and synchronisation in between,
 and every replay is checked against the eager result of the same call."""
 import numpy as np
@@ -10,7 +10,7 @@ import torch
 import oracle
 import workloads as W
 from workloads import device as D
-from gpu_util import announce, compare, to64
+from gpu_util import announce, compare
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -25,9 +25,8 @@ def decode(seed=91, batch=24, lo=300, hi=2500, W_=1024, g=4, d=128, hkv=8):
 
 
 CASES = {
-    "static one split": (lambda: decode(), {"schedule": "static", "num_splits": 1}),
-    "static split-K": (lambda: decode(), {"schedule": "static", "num_splits": 4}),
-    "dynamic": (lambda: decode(), {"schedule": "dynamic"}),
+    "one split": (lambda: decode(), {"num_splits": 1}),
+    "split-K": (lambda: decode(), {"num_splits": 4}),
     "block-sparse split-K": (lambda: W.make_block_sparse(
         name="bs_graph", seed=92, cache_lengths=[900, 2000, 300, 4100], rows=[1, 3, 1, 2], page_size=128,
         num_kv_heads=2, group=8, head_dim=128, dtype="e4m3", topk=5, block_size=64, scale=1 / np.sqrt(128)),
@@ -59,19 +58,11 @@ def test_graph_replays_match_eager(name):
             D.run(dc, options=opts, out=out, workspace=ws)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    dynamic = opts is not None and opts.get("schedule") == "dynamic"
     for k in range(4):
         announce("graph %s: replay %d" % (name, k))
         out.fill_(float("nan"))                      # eager work between replays
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        if dynamic:
-            # units land on either of a workgroup's two streams: agreement to rounding
-            compare(out, ref, tol, "graph %s replay %d" % (name, k))
-            assert np.abs(to64(out) - to64(eager)).max() <= 2e-2
-            counter = ws[ws.numel() - 256:ws.numel() - 252].view(torch.int32).item()
-            assert counter == 0, "work counter left at %d after replay %d" % (counter, k)
-        else:
-            assert torch.equal(out, eager), "replay %d differs from the eager call" % k
+        assert torch.equal(out, eager), "replay %d differs from the eager call" % k
     del g
