@@ -149,6 +149,26 @@ qsa_status qsa_sparse_attention(void *out, int32_t out_dtype, const qsa_ragged_q
                                 const qsa_launch_options *opts, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): qsa_sparse_attention without a workspace.
+ * Same arguments, checks, kernels and results as qsa_sparse_attention with the same
+ * options; the split-K partials (when the plan splits) go to a device array the
+ * library holds, QSA_NO_ALLOC_SCRATCH_BYTES on every GPU it runs on, from when the
+ * library's code is loaded there until the process ends. The call allocates and frees
+ * nothing. A call whose plan needs more scratch than that returns QSA_ERR_WORKSPACE
+ * before any launch (fewer splits or fewer rows per call fit). All calls on one GPU
+ * share its array: calls that can overlap on one GPU (different streams, or several
+ * threads) race and give undefined results; order them on one stream. The device
+ * current on the calling thread must be the one `stream` belongs to. Nothing in the
+ * array carries over from one call to the next. */
+#define QSA_NO_ALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+qsa_status qsa_sparse_attention_no_alloc(void *out, int32_t out_dtype, const qsa_ragged_q *q,
+                                         const qsa_paged_cache *kv, uint32_t layer_idx,
+                                         const int32_t *token_indices, int64_t selection_width,
+                                         const int32_t *counts, float scale,
+                                         const qsa_launch_options *opts, void *stream);
+
 /* ------------------------------------------------------------------------- */
 /* Block-sparse top-k attention ("Struct_msa_attention_ragged_paged").
  *

@@ -40,7 +40,7 @@ STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL", 2: "QSA_ERR_SHAPE", 3: "QSA_ERR_DTYPE"
 
 # Every function declared in include/qsa.h.
 EXPORTS = (
-    "qsa_sparse_attention_workspace_size", "qsa_sparse_attention",
+    "qsa_sparse_attention_workspace_size", "qsa_sparse_attention", "qsa_sparse_attention_no_alloc",
     "qsa_block_sparse_attention_workspace_size", "qsa_block_sparse_attention",
     "qsa_latent_sparse_attention_workspace_size", "qsa_latent_sparse_attention",
     "qsa_ragged_attention_workspace_size", "qsa_ragged_attention", "qsa_compress_keys",
@@ -93,6 +93,7 @@ def _load():
     pc, pr, po = ctypes.POINTER(_Cache), ctypes.POINTER(_Ragged), ctypes.POINTER(LaunchOptions)
     lib.qsa_sparse_attention_workspace_size.argtypes = [pr, pc, I64, po, ctypes.POINTER(SZ)]
     lib.qsa_sparse_attention.argtypes = [P, I32, pr, pc, ctypes.c_uint32, P, I64, P, F, po, P, SZ, P]
+    lib.qsa_sparse_attention_no_alloc.argtypes = [P, I32, pr, pc, ctypes.c_uint32, P, I64, P, F, po, P]
     lib.qsa_block_sparse_attention_workspace_size.argtypes = [pr, pc, I64, I64, po, ctypes.POINTER(SZ)]
     lib.qsa_block_sparse_attention.argtypes = [P, pr, pc, ctypes.c_uint32, P, I64, I64, F, P, P, po,
                                                P, SZ, P]
@@ -105,7 +106,7 @@ def _load():
     lib.qsa_compress_keys.argtypes = [P, I64, P, P, I32, I64, I64, P, pc, I64, U32, U32, I64, F, P]
     lib.qsa_select_blocks_workspace_size.argtypes = [pr, I64, I64, I64, U32, ctypes.POINTER(SZ)]
     lib.qsa_select_blocks.argtypes = [P, I64, P, P, pr, P, I64, P, U32, I64, I64, P, SZ, P]
-    for name in ("qsa_sparse_attention_workspace_size", "qsa_sparse_attention",
+    for name in ("qsa_sparse_attention_workspace_size", "qsa_sparse_attention", "qsa_sparse_attention_no_alloc",
                  "qsa_block_sparse_attention_workspace_size", "qsa_block_sparse_attention",
                  "qsa_latent_sparse_attention_workspace_size", "qsa_latent_sparse_attention",
                  "qsa_ragged_attention_workspace_size", "qsa_ragged_attention", "qsa_compress_keys",
@@ -253,6 +254,29 @@ def sparse_attention(q, input_row_offsets, kv: PagedCache, layer_idx: int, token
                                     ctypes.byref(ck), layer_idx, token_indices.data_ptr(), W,
                                     counts.data_ptr(), scale, o,
                                     ws.data_ptr() if ws is not None else None, wsb, _stream(q, stream)))
+    return out
+
+
+NO_ALLOC_SCRATCH_BYTES = 16 << 20    # QSA_NO_ALLOC_SCRATCH_BYTES
+
+
+def sparse_attention_no_alloc(q, input_row_offsets, kv: PagedCache, layer_idx: int, token_indices, counts,
+                              scale: float, *, out, max_prompt_length: int = 0, options=None,
+                              stream=None) -> torch.Tensor:
+    """sparse_attention without a workspace: split-K partials go to the library's own
+    device scratch (NO_ALLOC_SCRATCH_BYTES per GPU, shared by every such call on that
+    GPU: calls that may overlap on one GPU race). ``out`` is required, so the call
+    allocates nothing."""
+    _need_gpu(token_indices, counts, out)
+    _need_i32(token_indices, counts)
+    rq = _ragged(q, input_row_offsets, max_prompt_length)
+    ck = kv._c()
+    if out.shape != q.shape or out.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out must be %s of float32 or bfloat16" % (tuple(q.shape),))
+    W = token_indices.shape[1] if token_indices.dim() == 2 else 0
+    _check(lib.qsa_sparse_attention_no_alloc(out.data_ptr(), DTYPE_CODE[out.dtype], ctypes.byref(rq),
+                                             ctypes.byref(ck), layer_idx, token_indices.data_ptr(), W,
+                                             counts.data_ptr(), scale, _opts(options), _stream(q, stream)))
     return out
 
 

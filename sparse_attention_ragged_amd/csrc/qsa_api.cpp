@@ -165,6 +165,54 @@ qsa_status latent_plan(const qsa_ragged_q *q, int64_t window, int64_t num_comp,
     return plan_gather(q, 1, q->dtype, KEYS_LATENT, window + num_comp, 1, opts, plan);
 }
 
+// qsa_sparse_attention with a caller workspace, or (scratch = true) with the
+// library's own device scratch in place of one.
+qsa_status sparse_attention(void *out, int32_t out_dtype, const qsa_ragged_q *q, const qsa_paged_cache *kv,
+                            uint32_t layer_idx, const int32_t *token_indices, int64_t selection_width,
+                            const int32_t *counts, float scale, const qsa_launch_options *opts,
+                            void *workspace, size_t workspace_bytes, bool scratch, void *stream)
+{
+    Plan plan;
+    qsa_status s = sparse_plan(q, kv, selection_width, opts, &plan);
+    if (s != QSA_OK)
+        return s;
+    if ((s = check_out(out, out_dtype, q)) != QSA_OK)
+        return s;
+    if (layer_idx >= kv->num_layers)
+        return fail(QSA_ERR_SHAPE, "layer_idx %u >= num_layers %lld", layer_idx,
+                    (long long)kv->num_layers);
+    if (q->total_q > 0 && (!counts || (selection_width > 0 && !token_indices)))
+        return fail(QSA_ERR_NULL, "token_indices and counts are required");
+    if (!std::isfinite(scale))
+        return fail(QSA_ERR_SHAPE, "scale must be finite");
+    if (scratch) {
+        if (plan.ws_bytes > kNoAllocScratchBytes)
+            return fail(QSA_ERR_WORKSPACE, "this call needs %zu bytes of split-K scratch; the library's own "
+                                           "scratch holds %zu (use fewer splits, fewer rows per call, or "
+                                           "qsa_sparse_attention with a workspace)",
+                        plan.ws_bytes, kNoAllocScratchBytes);
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (plan.ws_bytes > 0 && q->total_q > 0) {
+            const int err = scratch_address(&workspace);
+            if (err)
+                return fail(QSA_ERR_HIP, "device scratch lookup failed: %s", hip_error_text(err));
+            workspace_bytes = kNoAllocScratchBytes;
+        }
+    } else if ((s = check_workspace(plan, workspace, workspace_bytes)) != QSA_OK) {
+        return s;
+    }
+    GatherParams p;
+    fill_common(p, out, out_dtype, q, kv->num_kv_heads, layer_idx, scale, plan, workspace);
+    p.kv = cache_addr(kv, layer_idx);
+    p.cache_lengths = kv->cache_lengths;
+    p.list_kind = KEYS_TOKEN_INDICES;
+    p.indices = token_indices;
+    p.counts = counts;
+    p.width = selection_width;
+    return run(p, plan, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -190,30 +238,19 @@ qsa_status qsa_sparse_attention(void *out, int32_t out_dtype, const qsa_ragged_q
                                 size_t workspace_bytes, void *stream)
 {
     clear_error();
-    Plan plan;
-    qsa_status s = sparse_plan(q, kv, selection_width, opts, &plan);
-    if (s != QSA_OK)
-        return s;
-    if ((s = check_out(out, out_dtype, q)) != QSA_OK)
-        return s;
-    if (layer_idx >= kv->num_layers)
-        return fail(QSA_ERR_SHAPE, "layer_idx %u >= num_layers %lld", layer_idx,
-                    (long long)kv->num_layers);
-    if (q->total_q > 0 && (!counts || (selection_width > 0 && !token_indices)))
-        return fail(QSA_ERR_NULL, "token_indices and counts are required");
-    if (!std::isfinite(scale))
-        return fail(QSA_ERR_SHAPE, "scale must be finite");
-    if ((s = check_workspace(plan, workspace, workspace_bytes)) != QSA_OK)
-        return s;
-    GatherParams p;
-    fill_common(p, out, out_dtype, q, kv->num_kv_heads, layer_idx, scale, plan, workspace);
-    p.kv = cache_addr(kv, layer_idx);
-    p.cache_lengths = kv->cache_lengths;
-    p.list_kind = KEYS_TOKEN_INDICES;
-    p.indices = token_indices;
-    p.counts = counts;
-    p.width = selection_width;
-    return run(p, plan, stream);
+    return sparse_attention(out, out_dtype, q, kv, layer_idx, token_indices, selection_width, counts, scale,
+                            opts, workspace, workspace_bytes, false, stream);
+}
+
+qsa_status qsa_sparse_attention_no_alloc(void *out, int32_t out_dtype, const qsa_ragged_q *q,
+                                         const qsa_paged_cache *kv, uint32_t layer_idx,
+                                         const int32_t *token_indices, int64_t selection_width,
+                                         const int32_t *counts, float scale,
+                                         const qsa_launch_options *opts, void *stream)
+{
+    clear_error();
+    return sparse_attention(out, out_dtype, q, kv, layer_idx, token_indices, selection_width, counts, scale,
+                            opts, nullptr, 0, true, stream);
 }
 
 qsa_status qsa_block_sparse_attention_workspace_size(const qsa_ragged_q *q, const qsa_paged_cache *kv,

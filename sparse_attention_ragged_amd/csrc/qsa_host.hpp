@@ -125,6 +125,14 @@ qsa_status plan_gather(const qsa_ragged_q *q, int64_t num_kv_heads, int32_t dtyp
                        Plan *plan);
 CacheAddr cache_addr(const qsa_paged_cache *c, uint32_t layer);
 
+// Size of the library-owned device scratch behind qsa_sparse_attention_no_alloc
+// (one copy per GPU, held until the process ends).
+constexpr size_t kNoAllocScratchBytes = QSA_NO_ALLOC_SCRATCH_BYTES;
+
+// Device address of the current device's scratch array (looked up once per device).
+// Returns a hipError_t value (0 = success).
+int scratch_address(void **ptr);
+
 // Launchers (qsa_*.hip). Return a hipError_t value (0 = success).
 int launch_gather_valu(const GatherParams &p, void *stream);
 int launch_gather_mfma(const GatherParams &p, void *stream);

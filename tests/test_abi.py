@@ -248,3 +248,22 @@ def test_select_blocks_checks(qsa):
     assert qsa.lib.qsa_select_blocks_workspace_size(ctypes.byref(q()), 640, 4, 512, 1000, ctypes.byref(n)) == 0
     assert n.value == 3 * 250 * 4
     assert call(qd=q(total_q=0)) == 0                                # nothing to do
+
+
+def test_no_alloc_refuses_plans_beyond_its_scratch(qsa):
+    """qsa_sparse_attention_no_alloc checks the plan's split-K partials against the
+    library's scratch size on the host and refuses larger plans before touching the
+    device (host buffers stand in for device pointers here)."""
+    f = qsa.lib.qsa_sparse_attention_no_alloc
+    q = ragged(total_q=5000, batch=2)
+    # 64 splits x 5000 rows x 8 heads x (128 + 2) fp32 = 1.3 GB of partials
+    big = qsa.LaunchOptions(64, 0, 0, 0)
+    assert f(P, 1, ctypes.byref(q), ctypes.byref(cache()), 0, P, 2048, P, 0.1, ctypes.byref(big), None) == 5
+    assert "scratch" in msg(qsa)
+    # the same argument checks as the workspace entry point
+    assert f(P, 1, ctypes.byref(q), ctypes.byref(cache()), 5, P, 2048, P, 0.1, None, None) == 2
+    assert f(P, 7, ctypes.byref(q), ctypes.byref(cache()), 0, P, 2048, P, 0.1, None, None) == 3
+    assert f(P, 1, ctypes.byref(q), ctypes.byref(cache()), 0, P, 2048, P, float("inf"), None, None) == 2
+    assert qsa.NO_ALLOC_SCRATCH_BYTES == 16 << 20
+    text = open(HEADER).read()
+    assert "#define QSA_NO_ALLOC_SCRATCH_BYTES ((size_t)16 << 20)" in text
