@@ -40,7 +40,7 @@ def test_latent_shapes(heads, d, out):
     case = latent_small(heads=heads, d=d, out=out)
     announce("latent heads=%d d=%d out=%s" % (heads, d, out))
     got, ref = run(case)
-    compare(got, ref, "bf16", "latent h=%d d=%d" % (heads, d), rel_rms_max=0.01)
+    compare(got, ref, "bf16", "latent h=%d d=%d" % (heads, d))
 
 
 @pytest.mark.parametrize("heads", [64, 16, 4])
@@ -73,21 +73,15 @@ def test_latent_large_sink_dominates():
     compare(got, ref, "bf16", "latent large sink")
 
 
-def test_c5_latent_full_size_sampled_rows():
+def test_c5_latent_full_size_all_rows():
     """The latent workload at full size (16 decode + 4 x 128 prefill rows, 64 heads,
-    head_dim 512) in the default launch configuration; the oracle checks every
-    decode row, 8 rows of each prefill sequence and the last 16 rows (528 rows fill
-    two rounds of 256 CUs plus 16: those 16 run split, the others unsplit)."""
+    head_dim 512) in the default launch configuration (528 rows fill two rounds of 256
+    CUs plus 16: those 16 run split, the others unsplit); the oracle checks every row."""
     announce("c5 full size: generating")
     case = W.c5_latent_bf16()
-    off = case.input_row_offsets.astype(np.int64)
-    rows = list(range(16))
-    for b in range(16, case.batch):
-        rows += [int(off[b]), int(off[b]) + 1] + [int(x) for x in np.linspace(off[b] + 2, off[b + 1] - 1, 6)]
-    rows = sorted(set(rows) | set(range(case.total_q - 16, case.total_q)))
-    announce("c5 full size: running (%d rows checked)" % len(rows))
-    got, ref = run(case, rows=rows)
-    compare(got, ref, "bf16", "c5 full", rel_rms_max=0.01)
+    announce("c5 full size: running (%d rows, all checked)" % case.total_q)
+    got, ref = run(case)
+    compare(got, ref, "bf16", "c5 full")
 
 
 @pytest.mark.parametrize("n_decode,tail", [(258, 2), (300, 44), (256 + 64, 64), (256 + 65, 65)])

@@ -40,7 +40,7 @@ def test_qsa_mfma_shapes(g, d, out):
     announce("qsa mfma g=%d d=%d out=%s" % (g, d, out))
     got, ref, _ = run(case)
     # tolerance of the input type (bf16): P is rounded to bf16 for the P.V product
-    compare(got, ref, "bf16", "mfma g=%d d=%d" % (g, d), rel_rms_max=0.01)
+    compare(got, ref, "bf16", "mfma g=%d d=%d" % (g, d))
 
 
 @pytest.mark.parametrize("splits,waves", [(1, 1), (1, 4), (3, 2), (8, 4)])
@@ -83,24 +83,14 @@ def test_qsa_mfma_counts_one_exact():
         assert torch.equal(out[r].cpu().view(torch.int16), v.view(torch.int16)), (r, pos[r])
 
 
-def test_c3_prefill_full_size_sampled_rows():
-    """The ragged-prefill workload at full size (8 sequences, ~9k rows, group 16) in the
-    default launch configuration; the oracle checks 192 rows spread over every
-    sequence, including each sequence's first and last row."""
+def test_c3_prefill_full_size_all_rows():
+    """The ragged-prefill workload at full size (8 sequences, ~9.7k rows, group 16) in
+    the default launch configuration; the oracle checks every row."""
     announce("c3 full size: generating")
     case = W.c3_prefill_bf16()
-    off = case.input_row_offsets.astype(np.int64)
-    rng = np.random.default_rng(0)
-    rows = set()
-    for b in range(case.batch):
-        if off[b + 1] > off[b]:
-            rows |= {int(off[b]), int(off[b + 1] - 1)}
-            rows |= set(rng.integers(off[b], off[b + 1], size=22).tolist())
-    rows = sorted(rows)
-    announce("c3 full size: running (%d rows checked)" % len(rows))
-    got, ref, out = run(case, rows=rows)
-    compare(got, ref, "bf16", "c3 full", rel_rms_max=0.01)
-    assert torch.isfinite(out.float()).all()
+    announce("c3 full size: running (%d rows, all checked)" % case.total_q)
+    got, ref, _ = run(case)
+    compare(got, ref, "bf16", "c3 full")
 
 
 # ----------------------------------------------------------------- block-sparse
@@ -136,16 +126,15 @@ def test_block_sparse_speculative_decode_full_size():
     case = W.c4s_block_sparse_spec_fp8()
     announce("block-sparse spec decode: running (%d rows)" % case.total_q)
     got, ref, _ = run(case)
-    compare(got, ref, "e4m3", "block-sparse spec decode", rel_rms_max=0.02)
+    compare(got, ref, "e4m3", "block-sparse spec decode")
 
 
-def test_block_sparse_prefill_sampled_rows():
-    """Block-sparse prefill: 4 sequences x 96 new tokens, bf16, sampled rows."""
+def test_block_sparse_prefill_all_rows():
+    """Block-sparse prefill: 4 sequences x 96 new tokens, bf16, every row."""
     case = W.c4p_block_sparse_prefill_bf16()
-    rows = sorted(set(np.linspace(0, case.total_q - 1, 40).astype(int).tolist()) | {95, 96, 191, 192})
-    announce("block-sparse prefill: running (%d rows checked)" % len(rows))
-    got, ref, _ = run(case, rows=rows)
-    compare(got, ref, "bf16", "block-sparse prefill", rel_rms_max=0.01)
+    announce("block-sparse prefill: running (%d rows)" % case.total_q)
+    got, ref, _ = run(case)
+    compare(got, ref, "bf16", "block-sparse prefill")
 
 
 def test_block_sparse_clip_never_reads_past_position():
@@ -162,5 +151,5 @@ def test_c4_block_sparse_full_size():
     case = W.c4_block_sparse_fp8()
     announce("c4 full size: running")
     got, ref, _ = run(case)
-    mx, rel = compare(got, ref, "e4m3", "c4 full", rel_rms_max=0.03)
+    mx, rel = compare(got, ref, "e4m3", "c4 full")
     announce("c4 max abs %.3e rel-rms %.3e" % (mx, rel))

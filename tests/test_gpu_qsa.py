@@ -15,7 +15,7 @@ import torch
 import oracle
 import workloads as W
 from workloads import device as D
-from gpu_util import TOL, announce, compare, to64
+from gpu_util import TOL, announce, compare, log_value, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +60,7 @@ def test_decode_small_bf16():
     case = small_decode()
     announce("decode small bf16")
     got, ref, _ = run_and_ref(case)
-    compare(got, ref, "bf16", "decode small", rel_rms_max=0.01)
+    compare(got, ref, "bf16", "decode small")
 
 
 @pytest.mark.parametrize("g,d,dtype,out", [(1, 64, "bf16", "f32"), (2, 256, "bf16", "bf16"),
@@ -184,10 +184,14 @@ def test_page_permutation_and_poison_are_bitwise_invariant():
     assert torch.equal(base, out3), "entries past counts were read"
 
 
-# fp32: the accumulation is fp32 throughout and only the order of additions changes.
-# bf16: the weights enter P.V rounded to bf16 relative to each split's own running
-# reference, so splits agree to the weights' rounding (2^-9 relative), not fp32's.
-@pytest.mark.parametrize("dtype,agree", [("f32", 2e-6), ("bf16", 4e-3)])
+# fp32: the accumulation is fp32 throughout and only the order of additions changes
+# (measured differences up to 1.2e-7). bf16: each weight enters P.V rounded to bf16
+# (relative error up to u = 2^-8) relative to its split's own running reference, so a
+# key's rounding differs between split counts. The output difference is then
+# sum_j w_j (e_j - e'_j) (v_j - out) / sum_j w_j with independent roundings e, e': about
+# u * rms(v - out) / sqrt(effective keys) in RMS (1e-4 here, out of outputs of RMS
+# 0.08) and measured up to 1.4e-3 at the largest of 16k outputs; 2.5e-3 bounds that.
+@pytest.mark.parametrize("dtype,agree", [("f32", 1e-6), ("bf16", 2.5e-3)])
 def test_splits_agree_and_runs_are_deterministic(dtype, agree):
     """Every split-K partition count gives the same result up to the rounding of its
     arithmetic, and repeated runs are bitwise identical."""
@@ -205,7 +209,9 @@ def test_splits_agree_and_runs_are_deterministic(dtype, agree):
         compare(a, ref, "f32" if dtype == "f32" else "bf16", "splits=%d" % s)
         outs[s] = to64(a)
     for s in (2, 3, 7, 16):
-        assert np.abs(outs[s] - outs[1]).max() <= agree, "split %d disagrees with one split" % s
+        diff = float(np.abs(outs[s] - outs[1]).max())
+        log_value("split agreement %s splits=%d" % (dtype, s), max_abs=diff, bound=agree)
+        assert diff <= agree, "split %d disagrees with one split (%.3e)" % (s, diff)
 
 
 @pytest.mark.parametrize("waves,unroll", [(1, 4), (2, 2), (4, 8), (8, 4), (3, 2)])
@@ -223,4 +229,4 @@ def test_c2_full_size_all_rows():
     case = W.c2_decode_bf16()
     announce("c2 full size: running")
     got, ref, _ = run_and_ref(case)
-    compare(got, ref, "bf16", "c2 full", rel_rms_max=0.01)
+    compare(got, ref, "bf16", "c2 full")
