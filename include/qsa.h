@@ -332,6 +332,16 @@ qsa_status qsa_select_blocks(int32_t *token_indices, int64_t selection_width, in
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------- */
+/* Measurement aid, not one of the operations above: a plain streaming read of `bytes`
+ * bytes at `src` (device, 16-byte aligned, bytes a multiple of 16), every byte loaded
+ * once with 16-byte loads by `grid` workgroups of 256 threads; workgroup i writes one
+ * word to sink[i] (device, `grid` words) so that the loads are kept. It is the
+ * reference against which the gather kernels' bandwidth is read on the same GPU, and
+ * a kernel of known traffic for scaling hardware byte counters. Asynchronous on
+ * `stream`; 1 <= grid <= 2^20. */
+qsa_status qsa_stream_read(const void *src, size_t bytes, uint32_t *sink, uint32_t grid, void *stream);
+
+/* ------------------------------------------------------------------------- */
 /* Text describing the last non-OK status returned on the calling thread. */
 const char *qsa_last_error(void);
 

@@ -45,7 +45,7 @@ EXPORTS = (
     "qsa_latent_sparse_attention_workspace_size", "qsa_latent_sparse_attention",
     "qsa_ragged_attention_workspace_size", "qsa_ragged_attention", "qsa_compress_keys",
     "qsa_select_blocks_workspace_size", "qsa_select_blocks",
-    "qsa_last_error", "qsa_abi_version", "qsa_struct_size", "qsa_set_timing_events",
+    "qsa_last_error", "qsa_abi_version", "qsa_struct_size", "qsa_set_timing_events", "qsa_stream_read",
 )
 
 
@@ -116,6 +116,8 @@ def _load():
     lib.qsa_abi_version.restype = I32
     lib.qsa_struct_size.argtypes = [I32]
     lib.qsa_struct_size.restype = SZ
+    lib.qsa_stream_read.argtypes = [P, SZ, P, U32, P]
+    lib.qsa_stream_read.restype = ctypes.c_int
     lib.qsa_set_timing_events.argtypes = [P, P]
     lib.qsa_set_timing_events.restype = None
     for i, st in enumerate((_Cache, _Ragged, LaunchOptions)):
@@ -417,6 +419,16 @@ def compress_keys(kv: PagedCache, key_counts, gamma, freqs_cis, layer_idx: int, 
                                  key_counts.data_ptr(), ctypes.byref(ck), batch, layer_idx, max_prompt_length,
                                  ratio, eps, _stream(kv.blocks, stream)))
     return out
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, grid: int = 2048, stream=None):
+    """Plain streaming read of every byte of ``src`` (a calibration kernel, not an
+    attention op); ``sink`` receives one int32 per workgroup (``grid`` of them)."""
+    _need_gpu(src, sink)
+    nbytes = src.numel() * src.element_size()
+    if sink.numel() * sink.element_size() < 4 * grid:
+        raise ValueError("sink must hold %d 32-bit words" % grid)
+    _check(lib.qsa_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), grid, _stream(src, stream)))
 
 
 def select_blocks_workspace_size(q_index, input_row_offsets, max_blocks: int, ratio: int, topk: int,

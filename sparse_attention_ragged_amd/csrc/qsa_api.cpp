@@ -622,6 +622,21 @@ qsa_status qsa_select_blocks(int32_t *token_indices, int64_t selection_width, in
     return QSA_OK;
 }
 
+qsa_status qsa_stream_read(const void *src, size_t bytes, uint32_t *sink, uint32_t grid, void *stream)
+{
+    clear_error();
+    if (grid < 1 || grid > (1u << 20))
+        return fail(QSA_ERR_SHAPE, "grid must be in [1, 2^20]");
+    if (!sink || (bytes > 0 && !src))
+        return fail(QSA_ERR_NULL, "src and sink are required");
+    if (!aligned16(src) || bytes % 16 != 0)
+        return fail(QSA_ERR_SHAPE, "src must be 16-byte aligned and bytes a multiple of 16");
+    const int err = launch_stream_read(src, bytes, sink, grid, stream);
+    if (err)
+        return fail(QSA_ERR_HIP, "HIP launch failed: %s", hip_error_text(err));
+    return QSA_OK;
+}
+
 void qsa_set_timing_events(void *start, void *stop)
 {
     t_ev_start = start;

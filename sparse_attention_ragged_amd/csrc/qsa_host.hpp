@@ -138,6 +138,7 @@ int launch_gather_valu(const GatherParams &p, void *stream);
 int launch_gather_mfma(const GatherParams &p, void *stream);
 int launch_gather_mfma_wide(const GatherParams &p, void *stream);
 int launch_splitk_combine(const GatherParams &p, void *stream);
+int launch_stream_read(const void *src, uint64_t bytes, void *sink, uint32_t grid, void *stream);
 int record_event(void *event, void *stream);
 const char *hip_error_text(int err);
 

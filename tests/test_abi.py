@@ -267,3 +267,13 @@ def test_no_alloc_refuses_plans_beyond_its_scratch(qsa):
     assert qsa.NO_ALLOC_SCRATCH_BYTES == 16 << 20
     text = open(HEADER).read()
     assert "#define QSA_NO_ALLOC_SCRATCH_BYTES ((size_t)16 << 20)" in text
+
+
+def test_stream_read_checks(qsa):
+    f = qsa.lib.qsa_stream_read
+    assert f(P, 1024, P, 0, None) == 2                 # grid >= 1
+    assert f(P, 1024, P, (1 << 20) + 1, None) == 2
+    assert f(P + 4, 1024, P, 8, None) == 2             # 16-byte alignment
+    assert f(P, 1000, P, 8, None) == 2                 # whole 16-byte chunks
+    assert f(P, 1024, None, 8, None) == 1
+    assert f(None, 1024, P, 8, None) == 1

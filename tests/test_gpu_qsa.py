@@ -230,3 +230,20 @@ def test_c2_full_size_all_rows():
     announce("c2 full size: running")
     got, ref, _ = run_and_ref(case)
     compare(got, ref, "bf16", "c2 full")
+
+
+def test_stream_read_loads_every_byte():
+    """The calibration read folds every 16-byte chunk into the workgroups' xors: the
+    xor of all sink words equals the xor of the buffer's words."""
+    import sparse_attention_ragged_amd as qsa
+    g = torch.Generator().manual_seed(5)
+    for nwords, grid in ((4 * 1000003, 97), (4 * 65536, 2048), (4, 3)):
+        host = torch.randint(-2 ** 31, 2 ** 31 - 1, (nwords,), generator=g, dtype=torch.int64).to(torch.int32)
+        src = host.to(DEV)
+        sink = torch.empty(grid, dtype=torch.int32, device=DEV)
+        announce("stream read %d words, grid %d" % (nwords, grid))
+        qsa.stream_read(src, sink, grid=grid)
+        torch.cuda.synchronize()
+        want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == want, (nwords, grid)
