@@ -376,6 +376,29 @@ __device__ __forceinline__ const char *row_address(const GatherParams &p, const 
     return present ? a : dummy;
 }
 
+// Stage 3 without the kv head term: byte address of k's plane-0 row of kv head 0 and
+// whether k is present (the caller adds head * head_dim * elem bytes, and uses the
+// address only when present).
+template <int EB, int LIST>
+__device__ __forceinline__ const char *row_base(const GatherParams &p, const KeyPos &k, uint32_t page, int32_t slot,
+                                                bool &present)
+{
+    if constexpr (LIST == KEYS_DENSE) {
+        present = k.present;
+        return static_cast<const char *>(p.dense_k) + (int64_t)k.tok * p.num_kv_heads * (int64_t)p.head_dim * EB;
+    }
+    bool in;
+    const char *a = leaf_row(p.kv, page, slot, 0u, in);
+    if constexpr (LIST == KEYS_LATENT) {
+        bool in_c;
+        const char *a_c = leaf_row(p.comp, page, slot, 0u, in_c);
+        a = k.comp ? a_c : a;
+        in = k.comp ? in_c : in;
+    }
+    present = k.present && in;
+    return a;
+}
+
 // Normalising factor of a finished softmax state (reference M, sum L, log2 domain):
 // out = acc * factor. With a sink logit (natural-log units, not scaled) the sink
 // joins the denominator once; a row with no keys is all zeros.
@@ -389,6 +412,42 @@ __device__ __forceinline__ float final_factor(const GatherParams &p, int64_t hea
         L = L * c + __builtin_amdgcn_exp2f(sl - M2);
     }
     return L > 0.f ? c / L : 0.f;
+}
+
+// ------------------------------------------------------------------ split-K merge
+//
+// Each split s leaves, per (row, q head), a log2-domain reference m_s, the sum
+// l_s = sum_j 2^(t_j - m_s) and acc_s = sum_j 2^(t_j - m_s) V_j. The exact result is
+//   out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,   M = max_s m_s
+// ("Struct_msa_attention_ragged_paged" design notes: partitioned KV bands merged by a
+// reduction), with the sink (latent attention) joining the denominator once; a (row,
+// head) that saw no key in any split is all zeros.
+
+__device__ __forceinline__ void store_out4(void *out, int32_t out_dtype, int64_t idx, f32x4_t v);
+
+// Merge of outputs d0 .. d0+3 of partial row `rel` (partials are indexed from row
+// split_row0 on) into the output of (row, head) `rh`; UNROLL partials' loads go out
+// together.
+template <int UNROLL = 8>
+__device__ __forceinline__ void merge_splits4(const GatherParams &p, int64_t rh, int64_t rel, int d0)
+{
+    const int S = p.num_splits;
+    const int D = p.head_dim;
+    const int64_t RH = (p.total_q - p.split_row0) * p.num_q_heads;
+    float M = kNoKey;
+#pragma unroll UNROLL
+    for (int s = 0; s < S; ++s)
+        M = fmaxf(M, p.ws_ml[((int64_t)s * RH + rel) * 2]);
+    float L = 0.f;
+    f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll UNROLL
+    for (int s = 0; s < S; ++s) {
+        const int64_t srh = (int64_t)s * RH + rel;
+        const float c = __builtin_amdgcn_exp2f(p.ws_ml[srh * 2] - M);
+        L += c * p.ws_ml[srh * 2 + 1];
+        a += c * *reinterpret_cast<const f32x4_t *>(p.ws_acc + srh * D + d0);
+    }
+    store_out4(p.out, p.out_dtype, rh * D + d0, a * final_factor(p, rh % p.num_q_heads, M, L));
 }
 
 // Four consecutive outputs (idx a multiple of 4): bf16 (round to nearest even) or fp32.

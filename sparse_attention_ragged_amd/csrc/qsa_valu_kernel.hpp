@@ -16,13 +16,16 @@
 //    page) with one request each, and the key's address is computed once per
 //    wavefront. Key slots take keys j0 + b*NK*U + u*NK + slot (batch b, u < U, NK slots
 //    per workgroup).
-//  * Address pipeline (the pages' `unroll` keys in flight, and more): while batch b
-//    is folded into the softmax state, the K/V rows of batch b+1 are in flight, the
-//    page-table entries of batch b+2 and the list entries of batch b+3. Every stage
-//    issues one load per key on every path (dummies for absent keys), so the compiler
-//    waits for exactly the oldest batch. There is no staging phase and no barrier
-//    before the first K/V load: a workgroup reaches full speed after three memory
-//    latencies.
+//  * Address staging: a workgroup walks its keys in chunks of kAddrPerThread keys
+//    per thread. For a chunk, every thread loads the list entries of its keys (all at
+//    once), then their page-table entries, and writes each key's row address (bit 0 =
+//    present) to LDS; one barrier later the chunk's rows stream. Absent keys (past the
+//    list, clipped, unused or outside the cache) read a harmless dummy row.
+//  * Row pipeline (the pages' `unroll`, gathered keys in flight before any is
+//    consumed): register sets of rows rotate, so that while batch b is folded into
+//    the softmax state the rows of batch b+1 (and b+2, with three sets for groups of
+//    1 or 2 heads) are in flight. The steady loop issues nothing but row loads, so
+//    the in-order memory counter waits for exactly the oldest batch.
 //  * Merge: teams of a wavefront merge with lane shuffles, wavefronts through LDS;
 //    the result is the normalised output row (one split) or an (m, l, acc) partial
 //    for the split-K combine kernel.
@@ -38,17 +41,30 @@ namespace qsa {
 namespace {
 
 constexpr int kMaxWaves = 8;
+// Keys whose row addresses each thread stages in LDS per chunk (8 bytes each): 16,
+// or 8 where fewer registers are left for the staging loads (the widened fp32 q rows
+// of four e4m3 heads; the two-leaf address choice of latent lists).
+constexpr int addr_per_thread(int dt, int g, int list)
+{
+    return (dt == QSA_FP8_E4M3 && g == 4) || list == KEYS_LATENT ? 8 : 16;
+}
 
 template <int DT, int D, int G, int U, int LIST>
 __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParams p)
 {
     using Core = ValuCore<DT, D, G, U>;
+    // register sets of rows: three (two batches in flight while one is folded) where
+    // the q rows and accumulators of the group leave room, else two
+    constexpr int kRowSets = G <= 2 ? 3 : 2;
+    constexpr int kAddrPerThread = addr_per_thread(DT, G, LIST);
     constexpr int EB = Core::EB;
     constexpr int EPC = Core::EPC;
     constexpr int CPL = Core::CPL;
     constexpr int TL = Core::TL;
     constexpr int TPW = Core::TPW;
-    extern __shared__ __attribute__((aligned(16))) float smem[];   // [NW][HB*G][2], then [NW][HB*G][D]
+    // LDS: the chunk's row addresses while streaming; afterwards the wavefronts' merge
+    // ([NW][HB*G][2] then [NW][HB*G][D] fp32)
+    extern __shared__ __attribute__((aligned(16))) float smem[];
 
     const int S = p.num_splits;
     const int HB = p.head_block;                 // kv heads of this workgroup, one team each
@@ -90,102 +106,122 @@ __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParam
     const int64_t j0 = (int64_t)s * p.split_keys;
     const int64_t jend = j0 + p.split_keys;
     const int64_t j1 = n < jend ? n : jend;
-    const int64_t per_batch = (int64_t)NK * U;
-    const int nb = j1 > j0 ? (int)((j1 - j0 + per_batch - 1) / per_batch) : 0;
+    const int per_batch = NK * U;
     const int64_t vdelta = LIST == KEYS_LATENT  ? 0
                            : LIST == KEYS_DENSE ? static_cast<const char *>(p.dense_v) - static_cast<const char *>(p.dense_k)
                                                 : (int64_t)p.kv.plane_stride_b;
     const char *dummy = qbase;                   // a readable row for absent keys
+    // the team's kv head within a key's row (the staged address is the head-0 row)
+    const int64_t head_off = LIST == KEYS_LATENT ? 0 : (int64_t)g * D * EB;
+    // list entries are per kv head only for block lists, which run one kv head per
+    // workgroup (head_block 1)
+    const int g_list = gb * HB;
 
     Core::widen_q(q);
     Core st;
     st.reset();
 
-    // ---- pipeline stages (each issues exactly one load per key on every path)
-    struct Entries { int32_t raw[U]; };
-    struct Pages { KeyPos k[U]; int32_t slot[U]; uint32_t page[U]; };
+    uint64_t *s_addr = reinterpret_cast<uint64_t *>(smem);   // [chunk]: row address | present
+    const int chunk = kAddrPerThread * nthreads;
     using Rows = typename Core::Rows;
 
-    auto key_index = [&](int batch, int u) -> int64_t {
-        return j0 + batch * per_batch + u * NK + wave * KPW + ks;
-    };
-    auto load_entries = [&](int batch, Entries &E) {
+    for (int64_t c0 = j0; c0 < j1; c0 += chunk) {
+        const int cn = (int)(j1 - c0 < chunk ? j1 - c0 : chunk);
+        // ---- stage this chunk's row addresses in LDS
+        lds_barrier();                           // every wavefront is done with the previous chunk's
+        {
+            int32_t raw[kAddrPerThread];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t jj = key_index(batch, u);
-            if constexpr (LIST == KEYS_DENSE)
-                E.raw[u] = 0;                      // dense: the key is its index, nothing to load
-            else
-                E.raw[u] = *entry_ptr<LIST>(p, r, g, jj, jj < j1);
-        }
-    };
-    auto load_pages = [&](int batch, const Entries &E, Pages &P) {
+            for (int k = 0; k < kAddrPerThread; ++k) {
+                const int t = tid + k * nthreads;
+                const int64_t jj = c0 + t;
+                if constexpr (LIST == KEYS_DENSE)
+                    raw[k] = 0;                  // dense: the key is its index, nothing to load
+                else
+                    raw[k] = *entry_ptr<LIST>(p, r, g_list, jj, t < cn);
+            }
+            KeyPos kp[kAddrPerThread];
+            int32_t slot[kAddrPerThread];
+            uint32_t page[kAddrPerThread];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t jj = key_index(batch, u);
-            P.k[u] = key_pos<LIST>(p, pos, jj, E.raw[u], jj < j1);
-            if constexpr (LIST == KEYS_DENSE) {
-                P.page[u] = 0;                     // dense: no page table
-                P.slot[u] = 0;
-            } else {
-                P.page[u] = *page_entry_ptr<LIST>(p, b, P.k[u], P.slot[u]);
+            for (int k = 0; k < kAddrPerThread; ++k) {
+                const int t = tid + k * nthreads;
+                kp[k] = key_pos<LIST>(p, pos, c0 + t, raw[k], t < cn);
+                if constexpr (LIST == KEYS_DENSE) {
+                    page[k] = 0;                 // dense: no page table
+                    slot[k] = 0;
+                } else {
+                    page[k] = *page_entry_ptr<LIST>(p, b, kp[k], slot[k]);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < kAddrPerThread; ++k) {
+                const int t = tid + k * nthreads;
+                if (t < cn) {
+                    bool ok;
+                    const char *a = row_base<EB, LIST>(p, kp[k], page[k], slot[k], ok);
+                    s_addr[t] = ok ? (reinterpret_cast<uint64_t>(a) | 1u) : 0u;
+                }
             }
         }
-    };
-    auto load_rows = [&](const Pages &P, Rows &R) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            bool ok;
-            const char *a = row_address<EB, LIST>(p, P.k[u], P.page[u], P.slot[u], g, dummy, ok);
-            R.ok[u] = ok;
-            const char *base = ok ? a : dummy;
-#pragma unroll
-            for (int c = 0; c < CPL; ++c)
-                R.k[u][c] = ldg16(base + (int64_t)Core::chunk_elem(c, ln) * EB);
-#pragma unroll
-            for (int c = 0; c < CPL; ++c)
-                R.v[u][c] = ldg16((ok ? a + vdelta : dummy) + (int64_t)Core::chunk_elem(c, ln) * EB);
-        }
-    };
-    auto consume = [&](const Rows &R) { st.consume(R, q, p.scale_log2); };
+        lds_barrier();
 
-    // ---- the pipeline: iteration i issues entries(i+2), pages(i+1), rows(i) and
-    // folds rows(i-1). Register sets alternate between even and odd iterations.
-    if (nb > 0) {
-        Entries E0, E1;
-        Pages P0, P1;
-        Rows R0, R1;
-        load_entries(0, E0);
-        load_entries(1, E1);
-        load_pages(0, E0, P0);
-        // iterations 0 and 1 are peeled so that the loop is entered with the same
-        // loads in flight as at its back edge
-        load_entries(2, E0);
-        load_pages(1, E1, P1);
-        load_rows(P0, R0);
-        load_entries(3, E1);
-        load_pages(2, E0, P0);
-        load_rows(P1, R1);
-        consume(R0);
-        for (int i = 2; i <= nb; i += 2) {
-            load_entries(i + 2, E0);
-            load_pages(i + 1, E1, P1);
-            load_rows(P0, R0);
-            consume(R1);
-            if (i + 1 > nb)
-                break;
-            load_entries(i + 3, E1);
-            load_pages(i + 2, E0, P0);
-            load_rows(P1, R1);
-            consume(R0);
+        // ---- stream the chunk's rows: batches b+1 and b+2 in flight while b is folded
+        const int nb = (cn + per_batch - 1) / per_batch;
+        auto issue = [&](int batch, Rows &R) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int t = batch * per_batch + u * NK + wave * KPW + ks;
+                const uint64_t e = s_addr[t < cn ? t : cn - 1];
+                const bool ok = t < cn && (e & 1u);
+                const char *a = ok ? reinterpret_cast<const char *>(e & ~(uint64_t)15) + head_off : dummy;
+                R.ok[u] = ok;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c)
+                    R.k[u][c] = ldg16(a + (int64_t)Core::chunk_elem(c, ln) * EB);
+#pragma unroll
+                for (int c = 0; c < CPL; ++c)
+                    R.v[u][c] = ldg16((ok ? a + vdelta : dummy) + (int64_t)Core::chunk_elem(c, ln) * EB);
+            }
+            // keep the fold of the previous batch below these loads: hoisted above them it
+            // would wait for that batch's rows before the next batch is issued
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // Whole loop bodies only (a batch past the end holds no key and folds nothing),
+        // so that the loop is entered and repeated with the same loads in flight.
+        if constexpr (kRowSets == 3) {
+            Rows R0, R1, R2;
+            issue(0, R0);
+            issue(1, R1);
+            for (int i = 0; i < nb; i += 3) {
+                issue(i + 2, R2);
+                st.consume(R0, q, p.scale_log2);
+                issue(i + 3, R0);
+                st.consume(R1, q, p.scale_log2);
+                issue(i + 4, R1);
+                st.consume(R2, q, p.scale_log2);
+            }
+        } else {
+            Rows R0, R1;
+            issue(0, R0);
+            for (int i = 0; i < nb; i += 2) {
+                issue(i + 1, R1);
+                st.consume(R0, q, p.scale_log2);
+                issue(i + 2, R0);
+                st.consume(R1, q, p.scale_log2);
+            }
         }
+        // (the loads of the batches past the chunk's end stay in flight: they read the
+        // dummy row and are waited for with the next chunk's entries or at the end)
     }
 
     // merge the key slots of this wavefront (teams of the same kv head sit TL*HB
     // lanes apart)
     st.merge_teams(TL * HB);
 
-    // merge the wavefronts through LDS: the key-slot-0 team of each kv head writes it
+    // merge the wavefronts through LDS (over the address chunk: every wavefront must be
+    // done reading it): the key-slot-0 team of each kv head writes its state
+    lds_barrier();
     const int HG = HB * G;                       // q heads of the workgroup
     float *s_ml = smem;                          // [NW][HG][2]
     float *s_acc = smem + ((NW * HG * 2 + 3) & ~3);   // [NW][HG][D], 16-byte aligned
@@ -206,7 +242,6 @@ __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParam
                                     st.acc[h][c * EPC + e + 3]);
         }
     }
-    // (the loads of the batches past the end that the pipeline issued stay in flight)
     lds_barrier();
     // each thread finishes two adjacent outputs
     for (int idx = tid; idx < HG * D / 2; idx += nthreads) {
@@ -249,7 +284,9 @@ int launch_valu(const GatherParams &p, void *stream)
         return (int)hipErrorInvalidConfiguration;
     // LDS of the cross-wavefront merge: (reference, sum) and D partial outputs per q head
     const size_t hg = (size_t)p.waves * p.head_block * G;
-    const size_t lds = (((2 * hg + 3) & ~(size_t)3) + hg * D) * sizeof(float);
+    const size_t merge = (((2 * hg + 3) & ~(size_t)3) + hg * D) * sizeof(float);
+    const size_t addrs = (size_t)addr_per_thread(DT, G, LIST) * 64 * p.waves * sizeof(uint64_t);
+    const size_t lds = merge > addrs ? merge : addrs;
     // allow more than the default dynamic LDS, once per device
     static std::atomic<uint64_t> raised{0};
     int dev = 0;

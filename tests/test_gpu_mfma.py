@@ -153,3 +153,28 @@ def test_c4_block_sparse_full_size():
     got, ref, _ = run(case)
     mx, rel = compare(got, ref, "e4m3", "c4 full")
     announce("c4 max abs %.3e rel-rms %.3e" % (mx, rel))
+
+
+def test_shared_workspace_across_plans_and_shapes():
+    """One workspace passed to split-K calls of different kernels, split counts and
+    shapes in a row (wavefront and matrix-core kernels, larger and smaller shapes):
+    nothing a call leaves in it changes a later call's result."""
+    cases = [
+        (block_small(seed=61, dtype="e4m3", cache=(900, 2000, 300, 4000)), {"num_splits": 4}),
+        (W.make_qsa(name="ws_valu", seed=62, rows=[1] * 5, cache_lengths=[300, 900, 1200, 40, 700], page_size=128,
+                    num_layers=1, layer_idx=0, num_kv_heads=2, group=4, head_dim=128, dtype="bf16",
+                    out_dtype="bf16", selection_width=512, selection="uniform_counts", scale=1 / np.sqrt(128)),
+         {"num_splits": 3}),
+        (block_small(seed=63, dtype="e4m3", rows=[2, 1, 3], cache=(700, 3000, 500), topk=6), {"num_splits": 7}),
+        (block_small(seed=64, dtype="e4m3", cache=(500, 260)), {"num_splits": 2}),
+        (prefill_small(seed=65, rows=(12, 5), cache=(400, 900), g=16, d=64, out="f32"), {"num_splits": 5}),
+        (block_small(seed=66, dtype="e4m3", cache=(900, 2000, 300, 4000)), {"num_splits": 4}),
+    ]
+    dcs = [(D.to_device(c, DEV), o) for c, o in cases]
+    ws = torch.full((max(D.workspace_size(dc, o) for dc, o in dcs),), 255, dtype=torch.uint8, device=DEV)
+    for k, ((case, _), (dc, opts)) in enumerate(zip(cases, dcs)):
+        announce("shared workspace call %d (%s, %s)" % (k, case.kind, opts))
+        out = D.run(dc, options=opts, workspace=ws)
+        torch.cuda.synchronize()
+        compare(out, oracle.run_case(case), "e4m3" if case.dtype == "e4m3" else
+                ("f32" if case.out_dtype == "f32" and case.dtype == "f32" else "bf16"), "shared workspace %d" % k)
