@@ -39,7 +39,7 @@ METRIC = "gathered-KV GB/s (% of HBM peak) + query-rows/s, bf16 decode config"
 HBM_PEAK_GBPS = 8000.0
 
 
-COUNTERS_SUMMARY = os.path.join(ROOT, "profiles", "gather_valu_c2_decode_bf16_counters.md")
+COUNTERS_SUMMARY = os.path.join(ROOT, "profiles", "gather_valu_c2_decode_bf16.md")
 
 
 # The sources that build and plan the C2 gather kernel (its translation unit with the
@@ -461,6 +461,9 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after warmup, run one device-to-device copy of this many MiB (a kernel "
                          "of known traffic for calibrating hardware byte counters)")
+    ap.add_argument("--stream-probe-mib", type=int, default=0,
+                    help="run one plain streaming read (qsa_stream_read) of this many MiB first: a "
+                         "read-only kernel of known traffic for calibrating hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run "
@@ -485,6 +488,14 @@ def main():
         torch.cuda.synchronize()
         log("copy probe: %d bytes read, %d bytes written" % (src.numel(), dst.numel()))
         del src, dst
+    if args.stream_probe_mib:
+        import sparse_attention_ragged_amd as qsa
+        src = torch.ones(args.stream_probe_mib << 20, dtype=torch.uint8, device=dev)
+        sink = torch.empty(2048, dtype=torch.int32, device=dev)
+        qsa.stream_read(src, sink, grid=2048, stream=stream)
+        torch.cuda.synchronize()
+        log("stream probe: %d bytes read" % src.numel())
+        del src, sink
     n_other = max(5, min(args.steps, 20))
     others = {
         "c3_prefill_bf16": lambda: other_workload("c3_prefill_bf16", W.c3_prefill_bf16, 1, dev, stream, n_other, 3),
