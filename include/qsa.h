@@ -93,7 +93,8 @@ typedef struct {
     const uint32_t *lookup_table; /* [batch, max_pages]: physical page of each logical page */
     int64_t max_pages;
     const uint32_t *cache_lengths; /* [batch]: keys cached before this step's rows */
-    uint32_t max_cache_length;     /* (host) max of cache_lengths; a sizing hint only */
+    uint32_t max_cache_length;     /* (host) max of cache_lengths, or 0 when not known; a sizing
+                                      hint (0 bounds nothing) */
     uint32_t reserved1;
 } qsa_paged_cache;
 
@@ -280,8 +281,9 @@ qsa_status qsa_ragged_attention(void *out, int32_t out_dtype, const qsa_ragged_q
  *                 of two in [16, 1024] bytes; kv->cache_lengths is part of the cache's
  *                 description and not read by this operation
  *   ratio >= 1, 0 <= rotary_dim <= head_dim (even), eps >= 0 (the pages' string eps)
- * Launch bound: when kv->max_cache_length + max_prompt_length (host) is non-zero,
- * blocks past (that sum) / ratio are not computed, so key_counts must not exceed it;
+ * Launch bound: when kv->max_cache_length (host) is non-zero, blocks past
+ * (kv->max_cache_length + max_prompt_length) / ratio are not computed, so key_counts
+ * must not exceed that sum (a max_cache_length of 0 gives no such bound);
  * freqs_cis must hold every position a computed block starts at (checked on the host).
  * A block whose positions or pages do not address the cache is not written.
  * No workspace; asynchronous on `stream`.
@@ -315,9 +317,10 @@ qsa_status qsa_compress_keys(void *block_keys, int64_t max_blocks, const void *g
  *   block_keys    [batch * max_blocks, head_dim] of q_index->dtype, 16-byte aligned (e.g.
  *                 qsa_compress_keys' block_keys); rows past a sequence's complete blocks
  *                 are never read
- *   cache_lengths [batch] (device); max_cache_length and q_index->max_prompt_length (host)
- *                 bound the candidates a launch covers when their sum is non-zero:
- *                 min(max_blocks, that sum / ratio) must be at most 32768
+ *   cache_lengths [batch] (device); when max_cache_length (host) is non-zero, it and
+ *                 q_index->max_prompt_length bound the candidates a launch covers:
+ *                 min(max_blocks, their sum / ratio) must be at most 32768; with
+ *                 max_cache_length 0, max_blocks itself must be
  *   selection_width >= topk * ratio + ratio - 1
  *   workspace     qsa_select_blocks_workspace_size bytes (fp32 scores), 16-byte aligned
  * Scores are fp32: blocks whose scores differ by less than fp32 rounding may be chosen

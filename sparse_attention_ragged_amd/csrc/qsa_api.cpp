@@ -96,8 +96,8 @@ qsa_status sparse_plan(const qsa_ragged_q *q, const qsa_paged_cache *kv, int64_t
     qsa_status s = check_cache(kv, "kv", 2);
     if (s == QSA_OK)
         s = check_q(q, kv, true);
-    if (s == QSA_OK && W < 0)
-        s = fail(QSA_ERR_SHAPE, "selection_width must be >= 0");
+    if (s == QSA_OK && (W < 0 || W > (int64_t(1) << 31)))
+        s = fail(QSA_ERR_SHAPE, "selection_width must be in [0, 2^31]");
     if (s == QSA_OK)
         s = plan_gather(q, kv->num_kv_heads, q->dtype, KEYS_TOKEN_INDICES, W, 1, opts, plan);
     return s;
@@ -116,7 +116,8 @@ qsa_status block_plan(const qsa_ragged_q *q, const qsa_paged_cache *kv, int64_t 
     if (s == QSA_OK && (block_size < 1 || kv->page_size % block_size != 0))
         s = fail(QSA_ERR_SHAPE, "block_size %lld must be >= 1 and divide page_size %lld",
                  (long long)block_size, (long long)kv->page_size);
-    if (s == QSA_OK && topk * block_size > (int64_t(1) << 30))
+    // (block_size divides page_size <= 2^30 here)
+    if (s == QSA_OK && (topk > (int64_t(1) << 30) || topk * block_size > (int64_t(1) << 30)))
         s = fail(QSA_ERR_SHAPE, "topk * block_size out of range");
     if (s == QSA_OK)
         s = plan_gather(q, kv->num_kv_heads, q->dtype, KEYS_BLOCKS, topk * block_size, block_size, opts, plan);
@@ -160,7 +161,7 @@ qsa_status latent_plan(const qsa_ragged_q *q, int64_t window, int64_t num_comp,
         return fail(QSA_ERR_SHAPE, "window must be >= 1");
     if (num_comp < 0)
         return fail(QSA_ERR_SHAPE, "num_comp must be >= 0");
-    if (window + num_comp > (int64_t(1) << 30))
+    if (window > (int64_t(1) << 30) || num_comp > (int64_t(1) << 30) || window + num_comp > (int64_t(1) << 30))
         return fail(QSA_ERR_SHAPE, "window + num_comp out of range");
     return plan_gather(q, 1, q->dtype, KEYS_LATENT, window + num_comp, 1, opts, plan);
 }
@@ -469,8 +470,9 @@ qsa_status qsa_compress_keys(void *block_keys, int64_t max_blocks, const void *g
     // (max_cache_length + max_prompt_length, when given) and the positions the page
     // table (and 31-bit positions) can address
     int64_t bound = max_blocks;
+    // (a max_cache_length of 0 says nothing about the cache: no bound from the hint then)
     const int64_t hint = (int64_t)kv->max_cache_length + (int64_t)max_prompt_length;
-    if (hint > 0)
+    if (kv->max_cache_length > 0)
         bound = std::min(bound, hint / ratio);
     const int64_t addressable = std::min(kv->max_pages * kv->page_size, (int64_t(1) << 31) - 1);
     bound = std::min(bound, addressable / ratio);
@@ -524,8 +526,10 @@ qsa_status qsa_compress_keys(void *block_keys, int64_t max_blocks, const void *g
 static int64_t select_bound(int64_t max_blocks, int64_t ratio, uint32_t max_cache_length, uint32_t max_prompt_length)
 {
     int64_t bound = max_blocks;
+    // the hint bounds the candidates only when it describes the cache (a max_cache_length
+    // of 0 gives no bound: the candidates are then limited by max_blocks alone)
     const int64_t hint = (int64_t)max_cache_length + (int64_t)max_prompt_length;
-    if (hint > 0 && hint / ratio < bound)
+    if (max_cache_length > 0 && hint / ratio < bound)
         bound = hint / ratio;
     return bound;
 }
@@ -548,12 +552,12 @@ static qsa_status select_check(const qsa_ragged_q *q, int64_t max_blocks, int64_
     if (ratio < 1 || ratio > (int64_t(1) << 20) || topk < 0 || topk > (int64_t(1) << 24) || max_blocks < 0)
         return fail(QSA_ERR_SHAPE, "ratio >= 1, topk >= 0 and max_blocks >= 0 are required");
     *bound = select_bound(max_blocks, ratio, max_cache_length, q->max_prompt_length);
+    if (*bound > kSelectMaxCandidates)
+        return fail(QSA_ERR_UNSUPPORTED, "at most %lld candidate blocks per row (max_blocks, or (max_cache_length "
+                                         "+ max_prompt_length) / ratio when max_cache_length > 0, is %lld)",
+                    (long long)kSelectMaxCandidates, (long long)*bound);
     if (q->total_q * ((*bound + 15) / 16) > (int64_t(1) << 31) - 1)
         return fail(QSA_ERR_SHAPE, "total_q * candidate blocks out of range");
-    if (*bound > kSelectMaxCandidates)
-        return fail(QSA_ERR_UNSUPPORTED, "at most %lld candidate blocks per row (min(max_blocks, (max_cache_length "
-                                         "+ max_prompt_length) / ratio) is %lld)",
-                    (long long)kSelectMaxCandidates, (long long)*bound);
     return QSA_OK;
 }
 

@@ -264,14 +264,6 @@ int launch_dt(const CompressParams &p, void *stream)
 
 }  // namespace
 
-bool compress_supported(int32_t dtype, int32_t head_dim)
-{
-    if (dtype != QSA_F32 && dtype != QSA_BF16)
-        return false;
-    const int64_t bytes = (int64_t)head_dim * (dtype == QSA_F32 ? 4 : 2);
-    return bytes >= 16 && bytes <= 1024 && bytes % 16 == 0 && ((bytes / 16) & (bytes / 16 - 1)) == 0;
-}
-
 int launch_compress_keys(const CompressParams &p, void *stream)
 {
     return p.dtype == QSA_BF16 ? launch_dt<QSA_BF16>(p, stream) : launch_dt<QSA_F32>(p, stream);

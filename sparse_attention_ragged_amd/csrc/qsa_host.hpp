@@ -142,7 +142,11 @@ int launch_stream_read(const void *src, uint64_t bytes, void *sink, uint32_t gri
 int record_event(void *event, void *stream);
 const char *hip_error_text(int err);
 
-// Which (dtype, group, head_dim) combinations have a built kernel.
+// Largest group of the head-split matrix-core kernel (16 heads per wavefront, four
+// score wavefronts).
+constexpr int kWideMaxGroup = 64;
+
+// Which (dtype, group, head_dim) combinations have a built kernel (qsa_support.cpp).
 bool valu_supported(int32_t dtype, int32_t group, int32_t head_dim);
 bool mfma_supported(int32_t dtype, int32_t group, int32_t head_dim);
 bool mfma_wide_supported(int32_t dtype, int32_t group, int32_t head_dim, int32_t list_kind);

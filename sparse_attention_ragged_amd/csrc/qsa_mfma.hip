@@ -389,12 +389,6 @@ int launch_mfma_t(const GatherParams &p, void *stream)
 
 }  // namespace
 
-bool mfma_supported(int32_t dtype, int32_t group, int32_t head_dim)
-{
-    return (dtype == QSA_BF16 || dtype == QSA_FP8_E4M3) && group >= 8 && group <= 16 &&
-           (head_dim == 64 || head_dim == 128 || head_dim == 256);
-}
-
 int launch_gather_mfma(const GatherParams &p, void *stream)
 {
     switch (p.list_kind) {

@@ -299,11 +299,6 @@ int launch_flash(const GatherParams &p, void *stream)
 
 }  // namespace
 
-bool mfma_flash_supported(int32_t dtype, int32_t group, int32_t head_dim)
-{
-    return dtype == QSA_BF16 && group >= 8 && group <= 16 && (head_dim == 64 || head_dim == 128 || head_dim == 256);
-}
-
 int launch_gather_mfma_flash(const GatherParams &p, void *stream)
 {
     switch (p.head_dim) {

@@ -37,6 +37,7 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 
 constexpr int kWaves = 4;             // head tiles (64 heads); one score + one value wavefront each
+static_assert(16 * kWaves == kWideMaxGroup, "the host-side support check assumes 64 heads per workgroup");
 constexpr int kWTile = 32;            // keys per tile
 constexpr int kDepth = 2;             // tiles of rows in flight
 constexpr int kXBufs = 3;             // LDS key tiles: being written, scored, accumulated
@@ -51,7 +52,6 @@ __device__ __forceinline__ bf16x8_t wide_bf16x8(u32x4 v)
     __builtin_memcpy(&r, &v, sizeof r);
     return r;
 }
-
 
 template <int D>
 __global__ void __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -182,7 +182,6 @@ gather_mfma_wide_kernel(GatherParams p)
             if (lane == 0)
                 s_ok[buf][wave] = bits;
         };
-
 
         // `xb`: the LDS key tile holding `tile`, tile % 3 (a compile-time constant in the
         // unrolled steps)
@@ -396,12 +395,6 @@ int launch_wide(const GatherParams &p, void *stream)
 }
 
 }  // namespace
-
-bool mfma_wide_supported(int32_t dtype, int32_t group, int32_t head_dim, int32_t list_kind)
-{
-    return dtype == QSA_BF16 && list_kind == KEYS_LATENT && group > 16 && group <= 16 * kWaves &&
-           (head_dim == 128 || head_dim == 256 || head_dim == 512);
-}
 
 int launch_gather_mfma_wide(const GatherParams &p, void *stream)
 {

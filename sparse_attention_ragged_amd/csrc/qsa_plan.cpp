@@ -25,7 +25,8 @@ constexpr int32_t kMaxSplits = 64;
 constexpr int64_t kWideSlots = 256;
 constexpr int64_t kMaxTailSplits = 8;
 
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// ceil(a / b) for a >= 0, b > 0, without forming a + b - 1 (which can overflow)
+int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0); }
 }  // namespace
 
 qsa_status fail(qsa_status code, const char *fmt, ...)
@@ -67,20 +68,27 @@ qsa_status check_cache(const qsa_paged_cache *c, const char *what, int64_t plane
     if (c->page_size > (1 << 30) || c->max_pages > (int64_t(1) << 31) ||
         c->num_pages > (int64_t(1) << 32))
         return fail(QSA_ERR_SHAPE, "%s: page_size, max_pages or num_pages out of range", what);
-    int64_t packed = c->num_planes * c->num_layers * c->page_size * c->num_kv_heads * c->head_dim;
+    // elements of a packed page, with the product checked: a page must stay below 4 GiB
+    int64_t packed = c->num_planes;
+    if (__builtin_mul_overflow(packed, c->num_layers, &packed) ||
+        __builtin_mul_overflow(packed, c->page_size, &packed) ||
+        __builtin_mul_overflow(packed, c->num_kv_heads, &packed) ||
+        __builtin_mul_overflow(packed, c->head_dim, &packed) || packed >= (int64_t(1) << 32))
+        return fail(QSA_ERR_UNSUPPORTED, "%s: pages of 4 GiB or more are not supported", what);
     if (c->page_stride != -1 && c->page_stride < packed)
         return fail(QSA_ERR_SHAPE, "%s: page_stride %lld is smaller than a packed page (%lld)", what,
                     (long long)c->page_stride, (long long)packed);
-    // every K/V row is fetched with 16-byte loads
+    // in-page offsets and the page stride are 32-bit byte quantities in the kernels
+    // (packed < 2^32 and head_dim <= packed, so the products below stay in range)
     const int64_t eb = elem_bytes(c->dtype);
     const int64_t stride = c->page_stride == -1 ? packed : c->page_stride;
+    if (stride >= (int64_t(1) << 32) || stride * eb >= (int64_t(1) << 32))
+        return fail(QSA_ERR_UNSUPPORTED, "%s: pages of 4 GiB or more (page_stride %lld elements) are not "
+                                         "supported", what, (long long)stride);
+    // every K/V row is fetched with 16-byte loads
     if (!aligned16(c->blocks) || (c->head_dim * eb) % 16 != 0 || (stride * eb) % 16 != 0)
         return fail(QSA_ERR_SHAPE, "%s: blocks, head_dim rows and page_stride must keep 16-byte "
                                    "alignment", what);
-    // in-page offsets and the page stride are 32-bit byte quantities in the kernels
-    if (stride * eb >= (int64_t(1) << 32))
-        return fail(QSA_ERR_UNSUPPORTED, "%s: pages of 4 GiB or more (page_stride %lld elements) are not "
-                                         "supported", what, (long long)stride);
     return QSA_OK;
 }
 

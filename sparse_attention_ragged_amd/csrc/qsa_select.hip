@@ -310,14 +310,6 @@ int launch_score(const SelectParams &p, hipStream_t s)
 
 }  // namespace
 
-bool select_supported(int32_t dtype, int32_t head_dim)
-{
-    if (dtype != QSA_F32 && dtype != QSA_BF16)
-        return false;
-    const int64_t bytes = (int64_t)head_dim * (dtype == QSA_F32 ? 4 : 2);
-    return bytes >= 16 && bytes <= 1024 && ((bytes / 16) & (bytes / 16 - 1)) == 0 && bytes % 16 == 0;
-}
-
 int launch_select_blocks(const SelectParams &p, void *stream, void *ev_start, void *ev_stop)
 {
     if (p.total_q == 0)

@@ -10,13 +10,6 @@ int launch_gather_valu_f32(const GatherParams &p, void *stream);
 int launch_gather_valu_bf16(const GatherParams &p, void *stream);
 int launch_gather_valu_e4m3(const GatherParams &p, void *stream);
 
-bool valu_supported(int32_t dtype, int32_t group, int32_t head_dim)
-{
-    return (dtype == QSA_F32 || dtype == QSA_BF16 || dtype == QSA_FP8_E4M3) &&
-           (group == 1 || group == 2 || group == 4) &&
-           (head_dim == 64 || head_dim == 128 || head_dim == 256);
-}
-
 int launch_gather_valu(const GatherParams &p, void *stream)
 {
     switch (p.dtype) {

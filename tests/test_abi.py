@@ -215,6 +215,9 @@ def test_compress_keys_checks(qsa):
     assert call(batch=0) == 0
     assert call(max_blocks=0) == 0
     assert call(kv=cache(num_kv_heads=1, max_cache_length=2, max_pages=4, page_size=16), mpl=1) == 0  # 3 / 4 = 0
+    # a max_cache_length of 0 bounds nothing: blocks up to min(16, 64 addressable / 4) = 16
+    # start at positions up to 60, so a 60-row table is refused again
+    assert call(kv=cache(num_kv_heads=1, max_cache_length=0, max_pages=4, page_size=16), mpl=1, npos=60) == 2
 
 
 def test_select_blocks_checks(qsa):
@@ -248,6 +251,10 @@ def test_select_blocks_checks(qsa):
     assert qsa.lib.qsa_select_blocks_workspace_size(ctypes.byref(q()), 640, 4, 512, 1000, ctypes.byref(n)) == 0
     assert n.value == 3 * 250 * 4
     assert call(qd=q(total_q=0)) == 0                                # nothing to do
+    # max_cache_length 0 says nothing about the cache: max_blocks alone bounds the candidates
+    assert qsa.lib.qsa_select_blocks_workspace_size(ctypes.byref(q()), 640, 4, 512, 0, ctypes.byref(n)) == 0
+    assert n.value == 3 * 640 * 4
+    assert call(max_blocks=40000, mcl=0) == 4                        # then max_blocks itself is checked
 
 
 def test_no_alloc_refuses_plans_beyond_its_scratch(qsa):

@@ -126,6 +126,30 @@ def test_select_max_blocks_cap():
     check_exact(case, run(case), "select cap")
 
 
+def test_select_without_max_cache_length():
+    """max_cache_length 0 (no hint): every complete block is still a candidate, and the
+    result equals the oracle's and the call with the hint."""
+    import sparse_attention_ragged_amd as qsa
+    case = W.make_select(name="sel_nohint", seed=74, rows=[1, 3, 2], cache_lengths=[300, 1200, 40], head_dim=128,
+                         dtype="bf16", ratio=4, topk=16, integer=True)
+    dc = D.select_to_device(case, DEV)
+    outs = []
+    for mcl in (0, int(np.max(case.cache_lengths))):
+        announce("select max_cache_length=%d" % mcl)
+        idx = torch.full((case.total_q, case.W), FILL, dtype=torch.int32, device=DEV)
+        counts = torch.full((case.total_q,), FILL, dtype=torch.int32, device=DEV)
+        blocks = torch.full((case.total_q, case.topk), FILL, dtype=torch.int32, device=DEV)
+        qsa.select_blocks(dc.q_index, dc.row_off, dc.block_keys, dc.cache_lengths, case.max_blocks, case.ratio,
+                          case.topk, selection_width=case.W, max_cache_length=mcl,
+                          max_prompt_length=case.max_prompt_length, token_indices=idx, counts=counts, blocks=blocks)
+        torch.cuda.synchronize()
+        got = (idx.cpu().numpy(), counts.cpu().numpy(), blocks.cpu().numpy())
+        check_exact(case, got, "select max_cache_length=%d" % mcl)
+        outs.append(got)
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+
+
 def test_select_full_size_indexer_workload():
     """Selection at the indexer workload's shapes (32 rows, 4k-8k candidate blocks of 4
     positions, top 511 blocks into 2047 positions)."""
