@@ -47,6 +47,7 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef const __attribute__((address_space(1))) u32x2 global_u32x2;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMfmaMaxWaves = 4;
 constexpr int kNumXcd = 8;            // XCDs of an MI355X; blocks are dealt to them round-robin
@@ -92,7 +93,7 @@ gather_mfma_kernel(GatherParams p)
     constexpr int NI = kTileKeys / KPI;         // load instructions per plane and tile
     constexpr int KROWB = RB + 32;              // LDS row of the K tile (bytes), padded
     constexpr int VROW = D + 16;                // LDS row of the V tile (bf16 elements), padded
-    constexpr int kWaveLds = kTileKeys * (KROWB + 2 * VROW);
+    constexpr int kWaveLds = kTileKeys * (KROWB + 2 * VROW + 16);   // + (K row, V row) address per key
     static_assert(D % 32 == 0 && LPK >= 1 && LPK <= 64 && kTileKeys % KPI == 0, "unsupported head_dim");
     using Chunk = typename std::conditional<DT == QSA_BF16, u32x4, u32x2>::type;
     __shared__ __attribute__((aligned(16))) char smem[kMfmaMaxWaves * kWaveLds];
@@ -122,6 +123,7 @@ gather_mfma_kernel(GatherParams p)
     const int lq = lane >> 4;
     char *s_k = smem + wave * kWaveLds;                                     // [32][KROWB] bytes
     uint16_t *s_v = reinterpret_cast<uint16_t *>(s_k + kTileKeys * KROWB);   // [32][VROW] bf16
+    u64x2 *s_rows = reinterpret_cast<u64x2 *>(s_k + kTileKeys * (KROWB + 2 * VROW));   // [32] row addresses
 
     // prologue: list length, sequence and the q fragments go out together
     int64_t n = LIST == KEYS_DENSE ? 0 : key_list_length(p, r);
@@ -160,16 +162,18 @@ gather_mfma_kernel(GatherParams p)
     for (int t = 0; t < NDT; ++t)
         acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Lane l (and l + 32) walks key l % 32 of each tile through the address pipeline;
-    // the rows are then loaded row-contiguous: load instruction i of a plane reads rows
-    // i*KPI .. i*KPI + KPI-1, LPK lanes per row, and every lane fetches its row's
-    // address from the lane that computed it.
+    // Lane l (and l + 32) walks key l % 32 of each tile through the address pipeline
+    // and leaves the key's K and V row addresses in the wavefront's LDS; the rows are
+    // then loaded row-contiguous: load instruction i of a plane reads rows
+    // i*KPI .. i*KPI + KPI-1, LPK lanes per row, every lane reading its row's addresses
+    // back from LDS (all reads in flight at once, one wait).
     const int kl = lane & 31;
     const int my_row = lane / LPK;              // row within a load instruction
     const int my_chunk = lane % LPK;            // 16-byte chunk within the row
     struct Entries { int32_t raw; };
     struct Pages { KeyPos k; int32_t slot; uint32_t page; };
     struct Rows { u32x4 k[NI], v[NI]; uint32_t present; };
+    const int chunk_b = my_chunk * 16;
 
     auto key_index = [&](int batch) -> int64_t { return j0 + (int64_t)batch * kTileKeys + kl; };
     auto load_entries = [&](int batch, Entries &E) {
@@ -193,16 +197,18 @@ gather_mfma_kernel(GatherParams p)
         bool ok;
         const char *a = row_address<EB, LIST>(p, P.k, P.page, P.slot, g, dummy, ok);
         R.present = (uint32_t)(__ballot(ok) & 0xffffffffull);
-        const char *own = ok ? a : dummy;
-        const uint32_t lo = (uint32_t)(uintptr_t)own, hi = (uint32_t)((uintptr_t)own >> 32);
+        // an absent key reads the q row for both planes (its weight is zero). The
+        // previous tile's reads of these slots came earlier in this wavefront's LDS order.
+        if (lane < kTileKeys)
+            s_rows[kl] = u64x2{(uint64_t)(uintptr_t)a, (uint64_t)(uintptr_t)(ok ? a + vdelta : dummy)};
+        u64x2 e[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            e[i] = s_rows[i * KPI + my_row];
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int src = i * KPI + my_row;
-            const uintptr_t ra = ((uintptr_t)(uint32_t)__shfl((int)hi, src) << 32) | (uint32_t)__shfl((int)lo, src);
-            const bool rok = (R.present >> src) & 1u;
-            const char *kaddr = reinterpret_cast<const char *>(ra) + my_chunk * 16;
-            R.k[i] = ldg16(kaddr);
-            R.v[i] = ldg16(rok ? kaddr + vdelta : dummy + my_chunk * 16);
+            R.k[i] = ldg16(reinterpret_cast<const char *>((uintptr_t)e[i].x) + chunk_b);
+            R.v[i] = ldg16(reinterpret_cast<const char *>((uintptr_t)e[i].y) + chunk_b);
         }
     };
     uint32_t present = 0u;                       // keys present in the staged tile
@@ -244,18 +250,26 @@ gather_mfma_kernel(GatherParams p)
                         as_long(*reinterpret_cast<const u32x2 *>(kp)), as_long(qf[c]), st[h], 0, 0, 0);
             }
         }
-        // scores in the log2 domain, absent keys at -inf
+        // scores in the log2 domain, absent keys (only in a tile that is not full) at -inf
         float sc[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sc[h][i] = st[h][i] * p.scale_log2;
+        if (present != 0xffffffffu) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sc[h][i] = (present >> (16 * h + 4 * lq + i)) & 1u ? sc[h][i] : kNegInf;
+        }
         float mx = m;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = 16 * h + 4 * lq + i;
-                const float v = st[h][i] * p.scale_log2;
-                sc[h][i] = (present >> key) & 1u ? v : kNegInf;
+            for (int i = 0; i < 4; ++i)
                 mx = fmaxf(mx, sc[h][i]);
-            }
         mx = xor32_max(xor16_max(mx));
         if (__any(mx > m + kSlack)) {
             const float alpha = __builtin_amdgcn_exp2f(m - mx);
