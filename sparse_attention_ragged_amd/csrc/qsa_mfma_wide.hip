@@ -101,9 +101,9 @@ gather_mfma_wide_kernel(GatherParams p)
     const int64_t j0 = (int64_t)s * p.split_keys;                 // 0 for an unsplit row
     const int64_t j1 = whole || n < j0 + p.split_keys ? n : j0 + p.split_keys;
     const int nb = j1 > j0 ? (int)((j1 - j0 + kWTile - 1) / kWTile) : 0;
-    // steps: nb scores, then the value step of the last tile; a whole number of loop
-    // trips so that register slots and LDS tiles stay static (extra steps idle)
-    const int nsteps = nb > 0 ? (nb + 1 + kUnroll - 1) / kUnroll * kUnroll : 0;
+    // steps: nb scores, then the value step of the last tile (the loop body is unrolled
+    // so that register slots and LDS tiles stay static, and leaves after step nb)
+    const int nsteps = nb > 0 ? nb + 1 : 0;
     const char *qrow0 = static_cast<const char *>(p.q) + (r * p.num_q_heads) * D * EB;
 
     const bool is_score = wave >= kWaves;
@@ -330,9 +330,11 @@ gather_mfma_wide_kernel(GatherParams p)
 
         // the steps; each role runs its own copy of the loop so that only its own state
         // is live in it. A store past the last tile writes a tile buffer nobody reads.
+        // Every wavefront of the workgroup leaves after the same step (nsteps is the
+        // workgroup's), so all pass the same barriers.
         static_assert(kUnroll % kDepth == 0 && kUnroll % kXBufs == 0, "static slots need a common period");
         auto steps = [&](auto &&work) {
-            for (int t = 0; t < nsteps; t += kUnroll) {
+            for (int t = 0;; t += kUnroll) {
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
                     const int tt = t + u;
@@ -343,6 +345,8 @@ gather_mfma_wide_kernel(GatherParams p)
                     E[k] = load_entry(tt + 1 + 3 * kDepth);          // entries of tt+1+3*DEPTH
                     work(tt, u);
                     lds_barrier();
+                    if (tt + 1 >= nsteps)
+                        return;
                 }
             }
         };
