@@ -14,16 +14,19 @@
 //    (A: transposing LDS reads of the key tile, B: P from LDS) and owns their output
 //    rows.
 //
-// All eight wavefronts also load: each walks its share of the keys of the split
+// The value wavefronts also load: each walks its share of the keys of the split
 // (window positions, then listed compressed entries) through the three-stage address
 // pipeline and writes its chunks of their latent rows into an LDS key tile. Per tile:
-// every wavefront stores its chunks of tile t+1 and issues loads, then score
-// wavefronts score tile t while value wavefronts accumulate tile t-1; one barrier,
-// which waits only for LDS traffic, ends the step (three LDS key tiles, two P
-// buffers). The vector-memory counter retires loads in issue order, so the three
-// address stages run DEPTH, 2*DEPTH and 3*DEPTH tiles ahead (rows, page-table
+// the value wavefronts store tile t+1 and issue loads, then score wavefronts score
+// tile t while value wavefronts accumulate tile t-1; one barrier, which waits only
+// for LDS traffic, ends the step (three LDS key tiles, two P buffers). The score
+// step is the longer one, so leaving the loading to the value wavefronts shortens
+// the step (measured at D 512: the score wavefronts' share of the loading sat on the
+// critical path). The vector-memory counter retires loads in issue order, so the
+// three address stages run DEPTH, 2*DEPTH and 3*DEPTH tiles ahead (rows, page-table
 // entries, list entries) and no step waits for anything newer than the tile it
-// stores. LDS operand reads are software-pipelined a few MFMAs ahead. The per-head
+// stores; DEPTH is one tile, all the value wavefronts' registers allow next to their
+// accumulators. LDS operand reads are software-pipelined a few MFMAs ahead. The per-head
 // sink logit joins the denominator once, at the final normalisation (here with one
 // split, in the combine kernel otherwise).
 #include "qsa_device.hpp"
@@ -39,7 +42,7 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 constexpr int kWaves = 4;             // head tiles (64 heads); one score + one value wavefront each
 static_assert(16 * kWaves == kWideMaxGroup, "the host-side support check assumes 64 heads per workgroup");
 constexpr int kWTile = 32;            // keys per tile
-constexpr int kDepth = 2;             // tiles of rows in flight
+constexpr int kDepth = 1;             // tiles of rows in flight (in the value wavefronts' registers)
 constexpr int kXBufs = 3;             // LDS key tiles: being written, scored, accumulated
 constexpr int kUnroll = 6;            // steps per loop trip: register slots and LDS tiles static
 constexpr float kWSlack = 8.0f;
@@ -72,9 +75,10 @@ gather_mfma_wide_kernel(GatherParams p)
     __shared__ uint32_t s_ok[kXBufs][2 * kWaves];   // presence bits of each wavefront's keys
     __shared__ float s_ml[kWaves][16][2];       // final (reference, sum) per head
 
-    // loading layout: TPK threads per key, each loading CPT chunks (chunk u*TPK + sub);
-    // wavefront w stages keys KPW*w .. KPW*w + KPW-1 of a tile
-    constexpr int TPK = kWThreads / kWTile;
+    // loading layout (value wavefronts only): TPK threads per key, each loading CPT
+    // chunks (chunk u*TPK + sub); value wavefront w stages keys KPW*w .. KPW*w + KPW-1
+    constexpr int kLoaders = 64 * kWaves;
+    constexpr int TPK = kLoaders / kWTile;
     constexpr int CPT = CHUNKS / TPK;
     constexpr int KPW = 64 / TPK;
     static_assert(CHUNKS % TPK == 0, "row chunks must split evenly over a key's threads");
@@ -229,7 +233,7 @@ gather_mfma_wide_kernel(GatherParams p)
             const uint16_t *x = s_x[xb];
             uint32_t present = 0;
 #pragma unroll
-            for (int w = 0; w < 2 * kWaves; ++w)
+            for (int w = 0; w < kWaves; ++w)
                 present |= s_ok[xb][w] << (w * KPW);
             // two chains per key half (even / odd 32-dim chunks) halve the MFMA dependency depth
             f32x4_t st[2], st2[2];
@@ -302,30 +306,32 @@ gather_mfma_wide_kernel(GatherParams p)
         int32_t E[kDepth];
         Page P[kDepth];
         Rows R[kDepth];
-        int32_t e_fill[3 * kDepth + 1];
+        if (!is_score) {
+            int32_t e_fill[3 * kDepth + 1];
 #pragma unroll
-        for (int j = 0; j <= 3 * kDepth; ++j)
-            e_fill[j] = load_entry(j);
-        b = find_seq_pos_wave(p.row_off, p.cache_lengths, p.batch, (uint32_t)r, pos);
-        Page p_fill[2 * kDepth + 1];
+            for (int j = 0; j <= 3 * kDepth; ++j)
+                e_fill[j] = load_entry(j);
+            b = find_seq_pos_wave(p.row_off, p.cache_lengths, p.batch, (uint32_t)r, pos);
+            Page p_fill[2 * kDepth + 1];
 #pragma unroll
-        for (int j = 0; j <= 2 * kDepth; ++j)
-            load_page(j, e_fill[j], p_fill[j]);
-        Rows r0;
-        load_rows(p_fill[0], r0);
+            for (int j = 0; j <= 2 * kDepth; ++j)
+                load_page(j, e_fill[j], p_fill[j]);
+            Rows r0;
+            load_rows(p_fill[0], r0);
 #pragma unroll
-        for (int j = 1; j <= kDepth; ++j)
-            load_rows(p_fill[j], R[j % kDepth]);
-        // steady-state registers before step t: R[j % DEPTH] holds the rows of tiles
-        // t+1 .. t+DEPTH, P[j % DEPTH] the page entries of t+1+DEPTH .. t+2*DEPTH and
-        // E[j % DEPTH] the list entries of t+1+2*DEPTH .. t+3*DEPTH
+            for (int j = 1; j <= kDepth; ++j)
+                load_rows(p_fill[j], R[j % kDepth]);
+            // steady-state registers before step t: R[j % DEPTH] holds the rows of tiles
+            // t+1 .. t+DEPTH, P[j % DEPTH] the page entries of t+1+DEPTH .. t+2*DEPTH and
+            // E[j % DEPTH] the list entries of t+1+2*DEPTH .. t+3*DEPTH
 #pragma unroll
-        for (int j = kDepth + 1; j <= 2 * kDepth; ++j)
-            P[j % kDepth] = p_fill[j];
+            for (int j = kDepth + 1; j <= 2 * kDepth; ++j)
+                P[j % kDepth] = p_fill[j];
 #pragma unroll
-        for (int j = 2 * kDepth + 1; j <= 3 * kDepth; ++j)
-            E[j % kDepth] = e_fill[j];
-        store_rows(r0, 0);
+            for (int j = 2 * kDepth + 1; j <= 3 * kDepth; ++j)
+                E[j % kDepth] = e_fill[j];
+            store_rows(r0, 0);
+        }
         lds_barrier();
 
         // the steps; each role runs its own copy of the loop so that only its own state
@@ -339,10 +345,12 @@ gather_mfma_wide_kernel(GatherParams p)
                 for (int u = 0; u < kUnroll; ++u) {
                     const int tt = t + u;
                     const int k = (u + 1) % kDepth;  // register slot of tiles tt+1 (+ multiples of DEPTH)
-                    store_rows(R[k], (u + 1) % kXBufs);              // tile tt+1 -> LDS tile (tt+1) % 3
-                    load_rows(P[k], R[k]);                           // rows of tt+1+DEPTH
-                    load_page(tt + 1 + 2 * kDepth, E[k], P[k]);      // pages of tt+1+2*DEPTH
-                    E[k] = load_entry(tt + 1 + 3 * kDepth);          // entries of tt+1+3*DEPTH
+                    if (!is_score) {
+                        store_rows(R[k], (u + 1) % kXBufs);          // tile tt+1 -> LDS tile (tt+1) % 3
+                        load_rows(P[k], R[k]);                       // rows of tt+1+DEPTH
+                        load_page(tt + 1 + 2 * kDepth, E[k], P[k]);  // pages of tt+1+2*DEPTH
+                        E[k] = load_entry(tt + 1 + 3 * kDepth);      // entries of tt+1+3*DEPTH
+                    }
                     work(tt, u);
                     lds_barrier();
                     if (tt + 1 >= nsteps)
