@@ -292,6 +292,60 @@ def stream_read_reference(dev, stream, nbytes=4 << 30, reps=10):
             "kernel": "qsa_stream_read: 16-byte nontemporal loads, 256-thread workgroups, 4 loads in flight per thread"}
 
 
+def key_row_offsets(case):
+    """Byte offsets, within the cache storage, of the K row (plane 0, the addressed layer)
+    of every (row, kv head, selected key) of a token-index case, in the gather kernel's
+    item order (row-major, kv head fastest); keys past a row's count are not listed."""
+    import numpy as np
+    kv = case.kv
+    H, D, ps = kv.num_kv_heads, kv.head_dim, kv.page_size
+    eb = 2 if case.dtype == "bf16" else (4 if case.dtype == "fp32" else 1)
+    W = case.token_indices.shape[1]
+    off = case.input_row_offsets.astype(np.int64)
+    items = case.total_q * H
+    offs = np.zeros((items, W), np.int64)
+    counts = np.zeros(items, np.int32)
+    for r in range(case.total_q):
+        b = int(np.searchsorted(off, r, side="right") - 1)
+        n = int(min(max(int(case.counts[r]), 0), W))
+        toks = case.token_indices[r, :n].astype(np.int64)
+        phys = kv.lookup_table[b][toks // ps].astype(np.int64)
+        base = phys * kv.page_elems + case.layer_idx * ps * H * D + (toks % ps) * H * D
+        for g in range(H):
+            offs[r * H + g, :n] = (base + g * D) * eb
+            counts[r * H + g] = n
+    plane_delta = kv.num_layers * ps * H * D * eb
+    return offs, counts, D * eb, plane_delta
+
+
+def address_replay_reference(case, dc, dev, stream, reps=10):
+    """Microseconds of the library's bare gather replay (qsa_gather_replay) over the
+    exact K/V rows the gather kernel reads for this call (same pool, same rows, same
+    workgroup per (row, kv head) and order), with no address computation or arithmetic:
+    what this access pattern itself reaches on this GPU."""
+    import numpy as np
+    import torch
+    import sparse_attention_ragged_amd as qsa
+    offs, counts, row_bytes, plane_delta = key_row_offsets(case)
+    d_offs = torch.from_numpy(offs).to(dev)
+    d_counts = torch.from_numpy(counts).to(dev)
+    sink = torch.empty(offs.shape[0] * 256, dtype=torch.int32, device=dev)
+    base = dc.kv.blocks
+    for _ in range(3):
+        qsa.gather_replay(base, d_offs, d_counts, row_bytes, plane_delta, sink, stream=stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        qsa.gather_replay(base, d_offs, d_counts, row_bytes, plane_delta, sink, stream=stream)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    nbytes = int(counts.astype(np.int64).sum()) * 2 * row_bytes
+    return {"us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "kv_bytes": nbytes,
+            "kernel": "qsa_gather_replay: the recorded K/V row offsets of this call, one 256-thread "
+                      "workgroup per (row, kv head), 16-byte row-contiguous loads, two batches in flight"}
+
+
 def other_workload(name, make, R, dev, stream, steps, warmup):
     import torch
     log("%s: generating" % name)
@@ -531,6 +585,8 @@ def main():
 
     # parity of the last timed output on every row (the oracle takes well under a second)
     par = parity(case, out)
+    log("address replay reference")
+    replay = address_replay_reference(case, calls[0], dev, stream)
 
     value = gathered / (ms_step * 1e-3) / 1e9
     achieved = a["algo_bytes"] / (kern_avg * 1e-3) / 1e9
@@ -567,6 +623,8 @@ def main():
                                "token-index list)",
                      "kernel_avg_us": round(kern_avg * 1e3, 3),
                      "frac_of_stream_read": round(achieved / stream_ref["GBps"], 4),
+                     "frac_of_address_replay": round(replay["us"] / (kern_avg * 1e3), 4),
+                     "address_replay": replay,
                      "algorithmic_bytes_per_launch": a["algo_bytes"], "unit_of_work": a["unit"],
                      "units_per_launch": a["units"], "bytes_per_unit": a["per_unit"],
                      "traffic_source": "rocprofv3 FETCH_SIZE + WRITE_SIZE per launch, scaled by a "

@@ -344,6 +344,24 @@ qsa_status qsa_select_blocks(int32_t *token_indices, int64_t selection_width, in
  * `stream`; 1 <= grid <= 2^20. */
 qsa_status qsa_stream_read(const void *src, size_t bytes, uint32_t *sink, uint32_t grid, void *stream);
 
+/* Measurement aid, not one of the operations above: a bare replay of a recorded
+ * gather. Workgroup i < items (256 threads) reads, for every j < counts[i] (clamped to
+ * [0, max_keys]), the row_bytes bytes at base + offsets[i * max_keys + j] and the
+ * row_bytes bytes plane_delta further on (the K and V rows of a key), with 16-byte
+ * loads laid out as in the gather kernels (row_bytes / 16 lanes per row, two batches of
+ * rows in flight per wavefront). A row whose bytes, in either plane, would fall outside
+ * [base, base + region_bytes) is skipped. Thread t of workgroup i writes a fold of its
+ * loads to sink[i * 256 + t] (device, items * 256 words). offsets (items * max_keys
+ * int64, byte offsets) and counts (items int32) are device arrays; base is device
+ * memory, 16-byte aligned, as is every offset. It gives the rate the access pattern
+ * itself reaches on this GPU, without address computation or arithmetic.
+ * row_bytes in {64, 128, 256, 512, 1024}; 1 <= max_keys <= 2^20; items <= 2^31 - 1;
+ * region_bytes >= row_bytes when items > 0 (skipped keys load the region's first row
+ * and do not fold it). Asynchronous on `stream`. */
+qsa_status qsa_gather_replay(const void *base, uint64_t region_bytes, const int64_t *offsets, const int32_t *counts,
+                             uint32_t items, uint32_t max_keys, uint32_t row_bytes, int64_t plane_delta,
+                             uint32_t *sink, void *stream);
+
 /* ------------------------------------------------------------------------- */
 /* Text describing the last non-OK status returned on the calling thread. */
 const char *qsa_last_error(void);

@@ -46,6 +46,7 @@ EXPORTS = (
     "qsa_ragged_attention_workspace_size", "qsa_ragged_attention", "qsa_compress_keys",
     "qsa_select_blocks_workspace_size", "qsa_select_blocks",
     "qsa_last_error", "qsa_abi_version", "qsa_struct_size", "qsa_set_timing_events", "qsa_stream_read",
+    "qsa_gather_replay",
 )
 
 
@@ -118,6 +119,8 @@ def _load():
     lib.qsa_struct_size.restype = SZ
     lib.qsa_stream_read.argtypes = [P, SZ, P, U32, P]
     lib.qsa_stream_read.restype = ctypes.c_int
+    lib.qsa_gather_replay.argtypes = [P, ctypes.c_uint64, P, P, U32, U32, U32, ctypes.c_int64, P, P]
+    lib.qsa_gather_replay.restype = ctypes.c_int
     lib.qsa_set_timing_events.argtypes = [P, P]
     lib.qsa_set_timing_events.restype = None
     for i, st in enumerate((_Cache, _Ragged, LaunchOptions)):
@@ -429,6 +432,25 @@ def stream_read(src: torch.Tensor, sink: torch.Tensor, grid: int = 2048, stream=
     if sink.numel() * sink.element_size() < 4 * grid:
         raise ValueError("sink must hold %d 32-bit words" % grid)
     _check(lib.qsa_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), grid, _stream(src, stream)))
+
+
+def gather_replay(base: torch.Tensor, offsets: torch.Tensor, counts: torch.Tensor, row_bytes: int,
+                  plane_delta: int, sink: torch.Tensor, stream=None):
+    """Bare replay of a recorded gather (a calibration kernel, not an attention op):
+    item i reads the ``row_bytes`` rows at byte offsets ``offsets[i, :counts[i]]`` of
+    ``base`` and the rows ``plane_delta`` bytes further on. ``offsets`` is int64
+    [items, max_keys], ``counts`` int32 [items]; ``sink`` receives 256 int32 per item."""
+    _need_gpu(base, offsets, counts, sink)
+    if offsets.dtype != torch.int64 or offsets.dim() != 2 or not offsets.is_contiguous():
+        raise ValueError("offsets must be a contiguous int64 [items, max_keys] tensor")
+    if counts.dtype != torch.int32 or counts.numel() != offsets.shape[0]:
+        raise ValueError("counts must be int32 with one entry per item")
+    items, max_keys = offsets.shape
+    if sink.numel() * sink.element_size() < 4 * 256 * items:
+        raise ValueError("sink must hold 256 32-bit words per item")
+    _check(lib.qsa_gather_replay(base.data_ptr(), base.numel() * base.element_size(), offsets.data_ptr(),
+                                 counts.data_ptr(), items, max_keys, row_bytes, plane_delta, sink.data_ptr(),
+                                 _stream(base, stream)))
 
 
 def select_blocks_workspace_size(q_index, input_row_offsets, max_blocks: int, ratio: int, topk: int,

@@ -641,6 +641,30 @@ qsa_status qsa_stream_read(const void *src, size_t bytes, uint32_t *sink, uint32
     return QSA_OK;
 }
 
+qsa_status qsa_gather_replay(const void *base, uint64_t region_bytes, const int64_t *offsets, const int32_t *counts,
+                             uint32_t items, uint32_t max_keys, uint32_t row_bytes, int64_t plane_delta,
+                             uint32_t *sink, void *stream)
+{
+    clear_error();
+    if (row_bytes != 64 && row_bytes != 128 && row_bytes != 256 && row_bytes != 512 && row_bytes != 1024)
+        return fail(QSA_ERR_SHAPE, "row_bytes must be 64, 128, 256, 512 or 1024");
+    if (max_keys < 1 || max_keys > (1u << 20))
+        return fail(QSA_ERR_SHAPE, "max_keys must be in [1, 2^20]");
+    if (items > 0x7fffffffu)
+        return fail(QSA_ERR_SHAPE, "items must be below 2^31");
+    if (items > 0 && (!base || !offsets || !counts || !sink))
+        return fail(QSA_ERR_NULL, "base, offsets, counts and sink are required");
+    if (!aligned16(base) || plane_delta % 16 != 0)
+        return fail(QSA_ERR_SHAPE, "base must be 16-byte aligned and plane_delta a multiple of 16");
+    if (items > 0 && region_bytes < row_bytes)
+        return fail(QSA_ERR_SHAPE, "region_bytes must hold at least one row");
+    const int err = launch_gather_replay(base, region_bytes, offsets, counts, items, max_keys, row_bytes,
+                                         plane_delta, sink, stream);
+    if (err)
+        return fail(QSA_ERR_HIP, "HIP launch failed: %s", hip_error_text(err));
+    return QSA_OK;
+}
+
 void qsa_set_timing_events(void *start, void *stop)
 {
     t_ev_start = start;

@@ -139,6 +139,9 @@ int launch_gather_mfma(const GatherParams &p, void *stream);
 int launch_gather_mfma_wide(const GatherParams &p, void *stream);
 int launch_splitk_combine(const GatherParams &p, void *stream);
 int launch_stream_read(const void *src, uint64_t bytes, void *sink, uint32_t grid, void *stream);
+int launch_gather_replay(const void *base, uint64_t region, const int64_t *offsets, const int32_t *counts,
+                         uint32_t items, uint32_t max_keys, uint32_t row_bytes, int64_t plane_delta, uint32_t *sink,
+                         void *stream);
 int record_event(void *event, void *stream);
 const char *hip_error_text(int err);
 

@@ -34,6 +34,12 @@ int launch_gather_mfma_wide(const GatherParams &p, void *) { check_gather(p); re
 int launch_gather_mfma_flash(const GatherParams &p, void *) { check_gather(p); return 0; }
 int launch_splitk_combine(const GatherParams &p, void *) { check_gather(p); return 0; }
 int launch_stream_read(const void *, uint64_t, void *, uint32_t, void *) { ++g_launches; return 0; }
+int launch_gather_replay(const void *, uint64_t, const int64_t *, const int32_t *, uint32_t, uint32_t, uint32_t, int64_t,
+                         uint32_t *, void *)
+{
+    ++g_launches;
+    return 0;
+}
 int launch_compress_keys(const CompressParams &p, void *)
 {
     if (p.batch < 1 || p.blocks_bound < 1)

@@ -276,6 +276,21 @@ def test_no_alloc_refuses_plans_beyond_its_scratch(qsa):
     assert "#define QSA_NO_ALLOC_SCRATCH_BYTES ((size_t)16 << 20)" in text
 
 
+def test_gather_replay_checks(qsa):
+    f = qsa.lib.qsa_gather_replay
+    assert f(P, 1 << 20, P, P, 4, 16, 200, 0, P, None) == 2        # row_bytes not a supported size
+    assert f(P, 1 << 20, P, P, 4, 0, 256, 0, P, None) == 2         # max_keys >= 1
+    assert f(P, 1 << 20, P, P, 4, (1 << 20) + 1, 256, 0, P, None) == 2
+    assert f(P, 1 << 20, P, P, 1 << 31, 16, 256, 0, P, None) == 2  # items below 2^31
+    assert f(P, 1 << 20, None, P, 4, 16, 256, 0, P, None) == 1
+    assert f(P, 1 << 20, P, None, 4, 16, 256, 0, P, None) == 1
+    assert f(P, 1 << 20, P, P, 4, 16, 256, 0, None, None) == 1
+    assert f(P + 4, 1 << 20, P, P, 4, 16, 256, 0, P, None) == 2    # 16-byte alignment
+    assert f(P, 1 << 20, P, P, 4, 16, 256, 8, P, None) == 2        # plane_delta a multiple of 16
+    assert f(P, 128, P, P, 4, 16, 256, 0, P, None) == 2            # region holds a row
+    assert f(None, 0, None, None, 0, 16, 256, 0, None, None) == 0  # no items: nothing to do
+
+
 def test_stream_read_checks(qsa):
     f = qsa.lib.qsa_stream_read
     assert f(P, 1024, P, 0, None) == 2                 # grid >= 1

@@ -232,6 +232,41 @@ def test_c2_full_size_all_rows():
     compare(got, ref, "bf16", "c2 full")
 
 
+def test_gather_replay_folds_every_listed_row():
+    """The address-replay calibration reads exactly the listed rows of both planes: the
+    xor of all sink words equals the xor of the words of every row j < counts[i] at
+    offsets[i, j] and offsets[i, j] + plane_delta; rows out of the region are skipped."""
+    import sparse_attention_ragged_amd as qsa
+    rng = np.random.default_rng(11)
+    for row_bytes, items, max_keys in ((256, 37, 300), (1024, 5, 70), (64, 9, 1000)):
+        region = 1 << 20
+        plane = region // 2
+        host = rng.integers(-2 ** 31, 2 ** 31 - 1, size=region // 4, dtype=np.int64).astype(np.int32)
+        base = torch.from_numpy(host).to(DEV)
+        nrows = plane // row_bytes
+        offs = (rng.integers(0, nrows, size=(items, max_keys)) * row_bytes).astype(np.int64)
+        counts = rng.integers(0, max_keys + 1, size=items).astype(np.int32)
+        counts[0] = max_keys
+        offs[1, 0] = region - row_bytes           # V row past the region: skipped
+        counts[1] = max(counts[1], 1)
+        sink = torch.empty(items * 256, dtype=torch.int32, device=DEV)
+        announce("gather replay %d B rows, %d items x %d" % (row_bytes, items, max_keys))
+        qsa.gather_replay(base, torch.from_numpy(offs).to(DEV), torch.from_numpy(counts).to(DEV), row_bytes,
+                          plane, sink)
+        torch.cuda.synchronize()
+        words = host.view(np.uint32)
+        want = np.uint32(0)
+        for i in range(items):
+            for j in range(counts[i]):
+                o = int(offs[i, j])
+                if o + plane + row_bytes > region:
+                    continue
+                want ^= np.bitwise_xor.reduce(words[o // 4:(o + row_bytes) // 4])
+                want ^= np.bitwise_xor.reduce(words[(o + plane) // 4:(o + plane + row_bytes) // 4])
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == want, (row_bytes, items, max_keys)
+
+
 def test_stream_read_loads_every_byte():
     """The calibration read folds every 16-byte chunk into the workgroups' xors: the
     xor of all sink words equals the xor of the buffer's words."""
