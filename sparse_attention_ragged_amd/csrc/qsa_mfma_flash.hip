@@ -116,16 +116,24 @@ gather_mfma_flash_kernel(GatherParams p)
     }
     const int nt = K1 > K0 ? (int)((K1 - K0 + kFlashTile - 1) / kFlashTile) : 0;
 
-    float m[RW], lsum[RW];                      // head li (shared by the 4 lanes of li)
-    f32x4_t acc[RW][NDT];
+    // softmax state per row: reference m (log2 units) of head li, the P.V accumulator
+    // and the running sum of the weights, kept by an MFMA with an all-ones A operand
+    // (every element of lsum[j] is the sum over the row's keys for head li, of the same
+    // bf16-rounded weights that P.V uses)
+    float m[RW];
+    f32x4_t acc[RW][NDT], lsum[RW];
 #pragma unroll
     for (int j = 0; j < RW; ++j) {
         m[j] = kNoKey;
-        lsum[j] = 0.f;
+        lsum[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < NDT; ++t)
             acc[j][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0 pairs
+    // with a positive scale the maximum of the scaled scores is the scaled maximum, so
+    // the scale is applied once to the maximum and folded into the exponent's FMA
+    const bool fold = p.scale_log2 > 0.f;
 
     // loading layout: wavefront w loads rows RPW*w .. RPW*w + RPW-1 of each tile
     const int my_row = lane / LPK;
@@ -184,24 +192,29 @@ gather_mfma_flash_kernel(GatherParams p)
         u32x4 pb[RW];
 #pragma unroll
         for (int j = 0; j < RW; ++j) {
-            float sc[2][4];
-            float mx = m[j];
             // key index relative to the row's first key; a tile wholly inside the
             // row's range (all but its first and last few) needs no mask
             const int64_t rel64 = t0 - first[j];
             const bool whole = rel64 >= 0 && rel64 + kFlashTile <= n[j];
-            const int32_t rel = (int32_t)(rel64 < -kFlashTile ? -kFlashTile : rel64 > n[j] ? n[j] : rel64);
-            const uint32_t nn = (uint32_t)n[j];
+            float sc[2][4];
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float v = st[j][h][i] * p.scale_log2;
-                    const uint32_t kr = (uint32_t)(rel + 16 * h + 4 * lq + i);
-                    sc[h][i] = whole || kr < nn ? v : kNegInf;
-                    mx = fmaxf(mx, sc[h][i]);
-                }
+                for (int i = 0; i < 4; ++i)
+                    sc[h][i] = fold ? st[j][h][i] : st[j][h][i] * p.scale_log2;
+            if (!whole) {
+                const int32_t rel = (int32_t)(rel64 < -kFlashTile ? -kFlashTile : rel64 > n[j] ? n[j] : rel64);
+                const uint32_t nn = (uint32_t)n[j];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        sc[h][i] = (uint32_t)(rel + 16 * h + 4 * lq + i) < nn ? sc[h][i] : kNegInf;
+            }
+            float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                             fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
             mx = xor32_max(xor16_max(mx));
+            mx = fmaxf(fold ? mx * p.scale_log2 : mx, m[j]);
             if (__any(mx > m[j] + kFlashSlack)) {
                 const float alpha = __builtin_amdgcn_exp2f(m[j] - mx);
                 lsum[j] *= alpha;
@@ -211,16 +224,16 @@ gather_mfma_flash_kernel(GatherParams p)
                 m[j] = mx;
             }
             float w[2][4];
+            const float sl = fold ? p.scale_log2 : 1.f;
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    w[h][i] = __builtin_amdgcn_exp2f(sc[h][i] - m[j]);
-                    lsum[j] += w[h][i];
-                }
+                for (int i = 0; i < 4; ++i)
+                    w[h][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[h][i], sl, -m[j]));
             // k-slot t < 4 is key 4q + t, t >= 4 is key 16 + 4q + t - 4
             pb[j] = u32x4{pack_bf16x2(w[0][0], w[0][1]), pack_bf16x2(w[0][2], w[0][3]),
                           pack_bf16x2(w[1][0], w[1][1]), pack_bf16x2(w[1][2], w[1][3])};
+            lsum[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ones), as_bf16x8(pb[j]), lsum[j], 0, 0, 0);
         }
         // V^T as the A operand via transposing LDS reads, shared by every row
         const int jr = li >> 2, qd = li & 3;
@@ -270,7 +283,7 @@ gather_mfma_flash_kernel(GatherParams p)
     // 16u + 4q .. 16u + 4q + 3 of head i
 #pragma unroll
     for (int j = 0; j < RW; ++j) {
-        const float ls = xor32_sum(xor16_sum(lsum[j]));
+        const float ls = lsum[j][0];
         if (row_real[j] && li < G) {
             const int64_t head = (int64_t)g * G + li;
             const int64_t rh = (r0 + RW * wave + j) * p.num_q_heads + head;
