@@ -161,6 +161,9 @@ gather_mfma_kernel(GatherParams p)
 #pragma unroll
     for (int t = 0; t < NDT; ++t)
         acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // with a positive scale the maximum of the scaled scores is the scaled maximum, so
+    // the scale is applied once to the maximum and folded into the exponent's FMA
+    const bool fold = p.scale_log2 > 0.f;
 
     // Lane l (and l + 32) walks key l % 32 of each tile through the address pipeline
     // and leaves the key's K and V row addresses in the wavefront's LDS; the rows are
@@ -250,13 +253,13 @@ gather_mfma_kernel(GatherParams p)
                         as_long(*reinterpret_cast<const u32x2 *>(kp)), as_long(qf[c]), st[h], 0, 0, 0);
             }
         }
-        // scores in the log2 domain, absent keys (only in a tile that is not full) at -inf
+        // scores (log2 domain once scaled), absent keys (only in a tile that is not full) at -inf
         float sc[2][4];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                sc[h][i] = st[h][i] * p.scale_log2;
+                sc[h][i] = fold ? st[h][i] : st[h][i] * p.scale_log2;
         if (present != 0xffffffffu) {
 #pragma unroll
             for (int h = 0; h < 2; ++h)
@@ -264,13 +267,10 @@ gather_mfma_kernel(GatherParams p)
                 for (int i = 0; i < 4; ++i)
                     sc[h][i] = (present >> (16 * h + 4 * lq + i)) & 1u ? sc[h][i] : kNegInf;
         }
-        float mx = m;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                mx = fmaxf(mx, sc[h][i]);
+        float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
         mx = xor32_max(xor16_max(mx));
+        mx = fmaxf(fold ? mx * p.scale_log2 : mx, m);
         if (__any(mx > m + kSlack)) {
             const float alpha = __builtin_amdgcn_exp2f(m - mx);
             lsum *= alpha;
@@ -280,11 +280,12 @@ gather_mfma_kernel(GatherParams p)
             m = mx;
         }
         float w[2][4];
+        const float sl = fold ? p.scale_log2 : 1.f;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                w[h][i] = __builtin_amdgcn_exp2f(sc[h][i] - m);
+                w[h][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[h][i], sl, -m));
                 lsum += w[h][i];
             }
         // P^T as the B operand: k-slot t < 4 is key 4q + t, t >= 4 is key 16 + 4q + t - 4

@@ -11,7 +11,8 @@
 //    (lazy rescale), leaving P (bf16, already in the MFMA operand layout) and the
 //    rescale factors in LDS;
 //  * value wavefront s accumulates O^T += X^T P^T for the same heads one tile later
-//    (A: transposing LDS reads of the key tile, B: P from LDS) and owns their output
+//    (A: transposing LDS reads of the key tile, B: P from LDS), and the sum of the
+//    weights with one more MFMA whose A operand is all ones, and owns their output
 //    rows.
 //
 // The value wavefronts also load: each walks its share of the keys of the split
@@ -73,7 +74,7 @@ gather_mfma_wide_kernel(GatherParams p)
     __shared__ float s_alpha[2][kWaves][16];    // rescale factor per head (when flagged)
     __shared__ uint32_t s_flag[2][kWaves];      // 1: the value wavefront rescales before adding
     __shared__ uint32_t s_ok[kXBufs][2 * kWaves];   // presence bits of each wavefront's keys
-    __shared__ float s_ml[kWaves][16][2];       // final (reference, sum) per head
+    __shared__ float s_m[kWaves][16];           // final reference per head
 
     // loading layout (value wavefronts only): TPK threads per key, each loading CPT
     // chunks (chunk u*TPK + sub); value wavefront w stages keys KPW*w .. KPW*w + KPW-1
@@ -189,15 +190,21 @@ gather_mfma_wide_kernel(GatherParams p)
 
         // `xb`: the LDS key tile holding `tile`, tile % 3 (a compile-time constant in the
         // unrolled steps)
-        auto accumulate = [&](int tile, int xb, f32x4_t *acc) {
+        // the value wavefront also keeps the running sum of the weights, by an MFMA with an
+        // all-ones A operand (every element of lsum is the sum over the keys, for head li,
+        // of the same bf16-rounded weights that P.V uses)
+        const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0 pairs
+        auto accumulate = [&](int tile, int xb, f32x4_t *acc, f32x4_t &lsum) {
             const int pb_buf = tile & 1;
             if (s_flag[pb_buf][hw]) {
                 const float alpha = s_alpha[pb_buf][hw][li];
+                lsum *= alpha;
 #pragma unroll
                 for (int t = 0; t < NDT; ++t)
                     acc[t] *= alpha;
             }
             const u32x4 pb = s_p[pb_buf][hw][lane];
+            lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wide_bf16x8(ones), wide_bf16x8(pb), lsum, 0, 0, 0);
             const uint16_t *x = s_x[xb];
             const int jr = li >> 2, qd = li & 3;
             // A = X^T for 16 dims x 32 keys: two transposing reads (keys 4q..4q+3 and
@@ -229,7 +236,10 @@ gather_mfma_wide_kernel(GatherParams p)
             }
         };
 
-        auto score = [&](int tile, int xb, const u32x4 *qf, float &m, float &lsum) {
+        // with a positive scale the maximum of the scaled scores is the scaled maximum, so
+        // the scale is applied once to the maximum and folded into the exponent's FMA
+        const bool fold = p.scale_log2 > 0.f;
+        auto score = [&](int tile, int xb, const u32x4 *qf, float &m) {
             const uint16_t *x = s_x[xb];
             uint32_t present = 0;
 #pragma unroll
@@ -266,22 +276,26 @@ gather_mfma_wide_kernel(GatherParams p)
             st[0] += st2[0];
             st[1] += st2[1];
             float sc[2][4];
-            float mx = m;
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = 16 * h + 4 * lq + i;
-                    const float v = st[h][i] * p.scale_log2;
-                    sc[h][i] = (present >> key) & 1u ? v : kNegInf;
-                    mx = fmaxf(mx, sc[h][i]);
-                }
+                for (int i = 0; i < 4; ++i)
+                    sc[h][i] = fold ? st[h][i] : st[h][i] * p.scale_log2;
+            if (present != 0xffffffffu) {        // absent keys (only in a tile that is not full) at -inf
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        sc[h][i] = (present >> (16 * h + 4 * lq + i)) & 1u ? sc[h][i] : kNegInf;
+            }
+            float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                             fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
             mx = xor32_max(xor16_max(mx));
+            mx = fmaxf(fold ? mx * p.scale_log2 : mx, m);
             const int pb_buf = tile & 1;
             uint32_t flag = 0;
             if (__any(mx > m + kWSlack)) {
                 const float alpha = __builtin_amdgcn_exp2f(m - mx);
-                lsum *= alpha;
                 m = mx;
                 if (lq == 0)
                     s_alpha[pb_buf][hw][li] = alpha;
@@ -290,13 +304,12 @@ gather_mfma_wide_kernel(GatherParams p)
             if (lane == 0)
                 s_flag[pb_buf][hw] = flag;
             float w[2][4];
+            const float sl = fold ? p.scale_log2 : 1.f;
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    w[h][i] = __builtin_amdgcn_exp2f(sc[h][i] - m);
-                    lsum += w[h][i];
-                }
+                for (int i = 0; i < 4; ++i)
+                    w[h][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[h][i], sl, -m));
             s_p[pb_buf][hw][lane] = u32x4{pack_bf16x2(w[0][0], w[0][1]), pack_bf16x2(w[0][2], w[0][3]),
                                           pack_bf16x2(w[1][0], w[1][1]), pack_bf16x2(w[1][2], w[1][3])};
         };
@@ -367,29 +380,26 @@ gather_mfma_wide_kernel(GatherParams p)
                 const u32x4 v = ldg16(qrow + (32 * c + 8 * lq) * EB);
                 qf[c] = head_real ? v : u32x4{0, 0, 0, 0};
             }
-            float m = kNoKey, lsum = 0.f;
+            float m = kNoKey;
             steps([&](int tt, int u) {
                 if (tt < nb)
-                    score(tt, u % kXBufs, qf, m, lsum);
+                    score(tt, u % kXBufs, qf, m);
             });
-            lsum = xor32_sum(xor16_sum(lsum));
-            if (lq == 0) {
-                s_ml[hw][li][0] = m;
-                s_ml[hw][li][1] = lsum;
-            }
+            if (lq == 0)
+                s_m[hw][li] = m;
             lds_barrier();
             return;
         }
-        f32x4_t acc[NDT];
+        f32x4_t acc[NDT], lsum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < NDT; ++t)
             acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         steps([&](int tt, int u) {
             if (tt >= 1 && tt <= nb)
-                accumulate(tt - 1, (u + kXBufs - 1) % kXBufs, acc);
+                accumulate(tt - 1, (u + kXBufs - 1) % kXBufs, acc, lsum);
         });
-        lds_barrier();                          // the score wavefronts' final state
-        finish(s_ml[hw][li][0], s_ml[hw][li][1], acc);
+        lds_barrier();                          // the score wavefronts' final reference
+        finish(s_m[hw][li], lsum[0], acc);
     }
 }
 
