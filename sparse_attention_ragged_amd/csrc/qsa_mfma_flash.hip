@@ -20,6 +20,8 @@
 // Compared with one wavefront per row walking its keys alone, the L2-to-LDS traffic and
 // the address work drop by the number of rows sharing a tile (8), and the LDS reads by
 // the rows per wavefront (2); the MFMA work is the same.
+#include <type_traits>
+
 #include "qsa_device.hpp"
 #include "qsa_flash_host.hpp"
 
@@ -132,8 +134,8 @@ gather_mfma_flash_kernel(GatherParams p)
     }
     const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0 pairs
     // with a positive scale the maximum of the scaled scores is the scaled maximum, so
-    // the scale is applied once to the maximum and folded into the exponent's FMA
-    const bool fold = p.scale_log2 > 0.f;
+    // the scale is applied once to the maximum and folded into the exponent's FMA (the
+    // tile loop is compiled for both cases and chosen once per call)
 
     // loading layout: wavefront w loads rows RPW*w .. RPW*w + RPW-1 of each tile
     const int my_row = lane / LPK;
@@ -161,7 +163,8 @@ gather_mfma_flash_kernel(GatherParams p)
             *reinterpret_cast<u32x4 *>(s_v + row * VROW + my_chunk * 8) = R.v[i];
         }
     };
-    auto consume = [&](int t, int buf) {
+    auto consume = [&](int t, int buf, auto fold_c) {
+        constexpr bool fold = decltype(fold_c)::value;
         const int64_t t0 = K0 + (int64_t)t * kFlashTile;
         bool any = false;
 #pragma unroll
@@ -259,7 +262,7 @@ gather_mfma_flash_kernel(GatherParams p)
     // rows and is never consumed), and every trip starts with the same two register sets
     // in flight, so the compiler's wait counts keep the newer tile's loads in flight
     // instead of draining them.
-    if (nt > 0) {
+    auto tiles = [&](auto fold_c) {
         Rows R0, R1;
         load_tile(0, R0);
         load_tile(1, R1);
@@ -267,16 +270,22 @@ gather_mfma_flash_kernel(GatherParams p)
             store_tile(0, R0);                    // tile t
             lds_barrier();
             load_tile(t + 2, R0);
-            consume(t, 0);
+            consume(t, 0, fold_c);
             store_tile(1, R1);                    // tile t + 1
             lds_barrier();
             if (t + 1 >= nt)
                 break;
             load_tile(t + 3, R1);
-            consume(t + 1, 1);
+            consume(t + 1, 1, fold_c);
             if (t + 2 >= nt)
                 break;
         }
+    };
+    if (nt > 0) {
+        if (p.scale_log2 > 0.f)
+            tiles(std::true_type());
+        else
+            tiles(std::false_type());
     }
 
     // per-head sums over the four lanes of each head; lane (i, q) stores dims
