@@ -91,7 +91,10 @@ gather_mfma_kernel(GatherParams p)
     constexpr int LPK = RB / 16;                // lanes that load one row (16 bytes each)
     constexpr int KPI = 64 / LPK;               // rows per load instruction
     constexpr int NI = kTileKeys / KPI;         // load instructions per plane and tile
-    constexpr int KROWB = RB + 32;              // LDS row of the K tile (bytes), padded
+    // LDS row of the K tile (bytes), padded so that the 16 rows one MFMA fragment read
+    // touches fall on distinct banks: bf16 reads 16 bytes a lane (row stride 72 dwords
+    // at D 128), e4m3 8 bytes (stride 36 dwords: 16 distinct multiples of 4 mod 64)
+    constexpr int KROWB = RB + (EB == 1 ? 16 : 32);
     constexpr int VROW = D + 16;                // LDS row of the V tile (bf16 elements), padded
     constexpr int kWaveLds = kTileKeys * (KROWB + 2 * VROW + 16);   // + (K row, V row) address per key
     static_assert(D % 32 == 0 && LPK >= 1 && LPK <= 64 && kTileKeys % KPI == 0, "unsupported head_dim");
