@@ -37,6 +37,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "gathered-KV GB/s (% of HBM peak) + query-rows/s, bf16 decode config"
 HBM_PEAK_GBPS = 8000.0
+# the secondary workloads each follow seconds of host-side input generation: their
+# warm-up runs until this much wall time has passed (the headline line keeps exactly
+# --warmup calls, after the reference reads and pool copies that precede it)
+OTHER_WARM_MS = 200.0
 
 
 COUNTERS_SUMMARY = os.path.join(ROOT, "profiles", "gather_valu_c2_decode_bf16.md")
@@ -198,7 +202,7 @@ def prepare(case, R, dev, opts):
     return calls, ws, out
 
 
-def time_steps(calls, opts, out, ws, stream, steps, warmup):
+def time_steps(calls, opts, out, ws, stream, steps, warmup, warm_ms=0.0):
     """Milliseconds per step over `steps` back-to-back calls (step k uses calls[k % R]),
     then the gather kernel's average milliseconds from the HIP events the library
     records around it, over a second pass of `steps` calls."""
@@ -208,20 +212,28 @@ def time_steps(calls, opts, out, ws, stream, steps, warmup):
     def step(k):
         D.run(calls[k % R], options=opts, out=out, workspace=ws, stream=stream)
 
-    return time_step_fn(step, steps, warmup)
+    return time_step_fn(step, steps, warmup, warm_ms)
 
 
-def time_step_fn(step, steps, warmup):
+def time_step_fn(step, steps, warmup, warm_ms=0.0):
     """For any step(k) callable that makes one library call: milliseconds per step over
     `steps` back-to-back calls (wall clock between two synchronisations); then the
     main kernel's average from the HIP events the library records around it, over a
     second pass; then each call's own duration from events around the whole call
-    (kernels and any combine step) over a third pass, as median, p10 and p90."""
+    (kernels and any combine step) over a third pass, as median, p10 and p90. With
+    warm_ms > 0 the warm-up goes on (past `warmup` calls) until that much wall time has
+    passed, so that a workload timed right after host-side input generation (the GPU
+    idle, its clocks down) is not timed while the clocks ramp up."""
     import numpy as np
     import torch
     import sparse_attention_ragged_amd as qsa
-    for k in range(warmup):
+    t_w = time.perf_counter()
+    k = 0
+    while k < warmup or (warm_ms > 0 and (time.perf_counter() - t_w) * 1e3 < warm_ms and k < 100000):
         step(k)
+        k += 1
+        if warm_ms > 0 and k % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
@@ -353,7 +365,7 @@ def other_workload(name, make, R, dev, stream, steps, warmup):
     a = algorithmic(case)
     calls, ws, out = prepare(case, R, dev, None)
     log("%s: timing %d steps (+ %d with kernel events, + %d with step events)" % (name, steps, steps, steps))
-    ms_step, kern, pct = time_steps(calls, None, out, ws, stream, steps, warmup)
+    ms_step, kern, pct = time_steps(calls, None, out, ws, stream, steps, warmup, OTHER_WARM_MS)
     log("%s: parity on every row" % name)
     par = parity(case, out)
     res = {"workload": name, "query_rows": case.total_q, "dtype": case.dtype,
@@ -390,7 +402,8 @@ def compress_workload(name, make, R, dev, stream, steps, warmup):
     out = torch.empty((case.batch * case.max_blocks, case.head_dim), dtype=W.TORCH_DTYPE[case.dtype], device=dev)
     torch.cuda.synchronize()
     log("%s: timing %d steps (+ %d with kernel events, + %d with step events)" % (name, steps, steps, steps))
-    ms_step, kern, pct = time_step_fn(lambda k: D.run_compress(calls[k % R], out=out, stream=stream), steps, warmup)
+    ms_step, kern, pct = time_step_fn(lambda k: D.run_compress(calls[k % R], out=out, stream=stream), steps, warmup,
+                                      OTHER_WARM_MS)
     nb = case.blocks_per_sequence()
     algo = W.compress_bytes(case)
     ref = oracle.run_case(case)
@@ -429,7 +442,7 @@ def select_workload(name, make, dev, stream, steps, warmup):
     torch.cuda.synchronize()
     log("%s: timing %d steps (+ %d with kernel events, + %d with step events)" % (name, steps, steps, steps))
     ms_step, kern, pct = time_step_fn(lambda k: D.run_select(dc, token_indices=idx, counts=counts, blocks=blocks,
-                                                             stream=stream), steps, warmup)
+                                                             stream=stream), steps, warmup, OTHER_WARM_MS)
     nv = case.candidates()
     eb = W.ELEM_BYTES[case.dtype]
     D_ = case.q_index.shape[1]
