@@ -26,6 +26,10 @@ constexpr uint32_t kBf16OnePair = 0x3F803F80u;
 // 16-byte load through the global address space (global_load_dwordx4 rather than a
 // flat load: the pointer came out of LDS, so the compiler cannot prove where it points).
 __device__ __forceinline__ u32x4 ldg16(const void *p) { return *(global_u32x4 *)(p); }
+// The same load marked non-temporal (streaming: the line is not kept for reuse). For
+// gathered rows that are read once per call this raised a bare replay of the decode
+// workload's rows from 5.6 to 6.5 TB/s on MI355X.
+__device__ __forceinline__ u32x4 ldg16_nt(const void *p) { return __builtin_nontemporal_load((global_u32x4 *)(p)); }
 
 // Two floats -> two bf16 (round to nearest even) packed in a dword, low half first.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)

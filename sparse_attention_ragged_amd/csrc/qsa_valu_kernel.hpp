@@ -178,10 +178,10 @@ __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParam
                 R.ok[u] = ok;
 #pragma unroll
                 for (int c = 0; c < CPL; ++c)
-                    R.k[u][c] = ldg16(a + (int64_t)Core::chunk_elem(c, ln) * EB);
+                    R.k[u][c] = ldg16_nt(a + (int64_t)Core::chunk_elem(c, ln) * EB);
 #pragma unroll
                 for (int c = 0; c < CPL; ++c)
-                    R.v[u][c] = ldg16((ok ? a + vdelta : dummy) + (int64_t)Core::chunk_elem(c, ln) * EB);
+                    R.v[u][c] = ldg16_nt((ok ? a + vdelta : dummy) + (int64_t)Core::chunk_elem(c, ln) * EB);
             }
             // keep the fold of the previous batch below these loads: hoisted above them it
             // would wait for that batch's rows before the next batch is issued
