@@ -355,7 +355,8 @@ def address_replay_reference(case, dc, dev, stream, reps=10):
     nbytes = int(counts.astype(np.int64).sum()) * 2 * row_bytes
     return {"us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "kv_bytes": nbytes,
             "kernel": "qsa_gather_replay: the recorded K/V row offsets of this call, one 256-thread "
-                      "workgroup per (row, kv head), 16-byte row-contiguous loads, two batches in flight"}
+                      "workgroup per (row, kv head), 16-byte non-temporal row-contiguous loads, two batches "
+                      "in flight"}
 
 
 def other_workload(name, make, R, dev, stream, steps, warmup):

@@ -348,8 +348,8 @@ qsa_status qsa_stream_read(const void *src, size_t bytes, uint32_t *sink, uint32
  * gather. Workgroup i < items (256 threads) reads, for every j < counts[i] (clamped to
  * [0, max_keys]), the row_bytes bytes at base + offsets[i * max_keys + j] and the
  * row_bytes bytes plane_delta further on (the K and V rows of a key), with 16-byte
- * loads laid out as in the gather kernels (row_bytes / 16 lanes per row, two batches of
- * rows in flight per wavefront). A row whose bytes, in either plane, would fall outside
+ * non-temporal loads laid out as in the decode gather kernel (row_bytes / 16 lanes per
+ * row, two batches of rows in flight per wavefront). A row whose bytes, in either plane, would fall outside
  * [base, base + region_bytes) is skipped. Thread t of workgroup i writes a fold of its
  * loads to sink[i * 256 + t] (device, items * 256 words). offsets (items * max_keys
  * int64, byte offsets) and counts (items int32) are device arrays; base is device

@@ -52,8 +52,9 @@ __global__ void __launch_bounds__(kStreamThreads) stream_read_kernel(const u32x4
 // Replay of a recorded gather: workgroup i (four wavefronts) reads, for each j < counts[i],
 // the row of RB bytes at base + offsets[i * max_keys + j] and the one plane_delta bytes
 // further, with the row-contiguous 16-byte loads of the gather kernels (LPR lanes per
-// row, 64 / LPR rows per wave instruction, four instructions per plane and batch) and
-// two batches in flight per wavefront. Keys are dealt to the wavefronts in batches.
+// row, 64 / LPR rows per wave instruction, four instructions per plane and batch, marked
+// non-temporal like the decode kernel's row loads) and two batches in flight per
+// wavefront. Keys are dealt to the wavefronts in batches.
 // A row whose bytes (either plane) would leave [base, base + region) is skipped.
 template <int RB>
 __global__ void __launch_bounds__(256) gather_replay_kernel(const char *base, uint64_t region, const int64_t *offsets,
@@ -91,8 +92,8 @@ __global__ void __launch_bounds__(256) gather_replay_kernel(const char *base, ui
             ok[slot][i] = in;
             const char *kr = in ? base + o[i] : base;
             const char *vr = in ? base + o[i] + plane_delta : base;
-            k[slot][i] = *reinterpret_cast<const u32x4 *>(kr + chunk * 16);
-            v[slot][i] = *reinterpret_cast<const u32x4 *>(vr + chunk * 16);
+            k[slot][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kr + chunk * 16));
+            v[slot][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vr + chunk * 16));
         }
     };
     if (nb > 0)
