@@ -45,6 +45,7 @@ void fill_common(GatherParams &p, void *out, int32_t out_dtype, const qsa_ragged
     p.split_keys = plan.split_keys;
     p.split_row0 = plan.split_row0;
     p.head_block = plan.head_block;
+    p.stream_rows = plan.stream_rows;
     if (plan.num_splits > 1) {
         p.ws_acc = static_cast<float *>(ws);
         p.ws_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + plan.ws_ml_offset);

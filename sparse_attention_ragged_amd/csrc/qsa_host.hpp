@@ -82,6 +82,7 @@ struct GatherParams {
     int64_t split_keys;              // keys per split (in key-list units)
     int64_t split_row0;              // rows before it run unsplit (head-split kernel's tail plan)
     int32_t head_block;              // wavefront kernel: kv heads one workgroup covers
+    int32_t stream_rows;             // wavefront kernel: K/V row loads non-temporal (rows read once)
     float *ws_acc;                   // [S, total_q, Hq, D] when num_splits > 1
     float *ws_ml;                    // [S, total_q, Hq, 2]
 };
@@ -101,6 +102,7 @@ struct Plan {
     int64_t split_keys;
     int64_t split_row0;     // rows before it run unsplit; the rest num_splits ways (0: all rows)
     int32_t head_block;     // wavefront kernel: kv heads per workgroup (1 for other paths)
+    int32_t stream_rows;    // wavefront kernel: K/V row loads non-temporal
     size_t ws_bytes;
     size_t ws_ml_offset;
 };

@@ -49,7 +49,9 @@ constexpr int addr_per_thread(int dt, int g, int list)
     return (dt == QSA_FP8_E4M3 && g == 4) || list == KEYS_LATENT ? 8 : 16;
 }
 
-template <int DT, int D, int G, int U, int LIST>
+// NT: the K/V row loads are non-temporal (chosen by the planner for calls whose rows
+// are read once: one query row per sequence)
+template <int DT, int D, int G, int U, int LIST, bool NT>
 __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParams p)
 {
     using Core = ValuCore<DT, D, G, U>;
@@ -177,11 +179,15 @@ __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParam
                 const char *a = ok ? reinterpret_cast<const char *>(e & ~(uint64_t)15) + head_off : dummy;
                 R.ok[u] = ok;
 #pragma unroll
-                for (int c = 0; c < CPL; ++c)
-                    R.k[u][c] = ldg16_nt(a + (int64_t)Core::chunk_elem(c, ln) * EB);
+                for (int c = 0; c < CPL; ++c) {
+                    const char *ka = a + (int64_t)Core::chunk_elem(c, ln) * EB;
+                    R.k[u][c] = NT ? ldg16_nt(ka) : ldg16(ka);
+                }
 #pragma unroll
-                for (int c = 0; c < CPL; ++c)
-                    R.v[u][c] = ldg16_nt((ok ? a + vdelta : dummy) + (int64_t)Core::chunk_elem(c, ln) * EB);
+                for (int c = 0; c < CPL; ++c) {
+                    const char *va = (ok ? a + vdelta : dummy) + (int64_t)Core::chunk_elem(c, ln) * EB;
+                    R.v[u][c] = NT ? ldg16_nt(va) : ldg16(va);
+                }
             }
             // keep the fold of the previous batch below these loads: hoisted above them it
             // would wait for that batch's rows before the next batch is issued
@@ -274,8 +280,8 @@ __global__ void __launch_bounds__(64 * kMaxWaves) gather_valu_kernel(GatherParam
     }
 }
 
-template <int DT, int D, int G, int U, int LIST>
-int launch_valu(const GatherParams &p, void *stream)
+template <int DT, int D, int G, int U, int LIST, bool NT>
+int launch_valu_nt(const GatherParams &p, void *stream)
 {
     const int64_t grid = p.total_q * (int64_t)(p.num_kv_heads / p.head_block) * p.num_splits;
     if (grid <= 0)
@@ -293,15 +299,27 @@ int launch_valu(const GatherParams &p, void *stream)
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         dev = 63;
     if (!(raised.load() >> dev & 1u)) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gather_valu_kernel<DT, D, G, U, LIST>),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gather_valu_kernel<DT, D, G, U, LIST, NT>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess)
             return (int)e;
         raised.fetch_or(uint64_t(1) << dev);
     }
-    hipLaunchKernelGGL((gather_valu_kernel<DT, D, G, U, LIST>), dim3((unsigned)grid), dim3(64 * p.waves),
+    hipLaunchKernelGGL((gather_valu_kernel<DT, D, G, U, LIST, NT>), dim3((unsigned)grid), dim3(64 * p.waves),
                        lds, static_cast<hipStream_t>(stream), p);
     return (int)hipGetLastError();
+}
+
+// non-temporal row loads only exist for the index lists (dense and latent rows are
+// shared by neighbouring rows)
+template <int DT, int D, int G, int U, int LIST>
+int launch_valu(const GatherParams &p, void *stream)
+{
+    if constexpr (LIST == KEYS_TOKEN_INDICES || LIST == KEYS_BLOCKS) {
+        if (p.stream_rows)
+            return launch_valu_nt<DT, D, G, U, LIST, true>(p, stream);
+    }
+    return launch_valu_nt<DT, D, G, U, LIST, false>(p, stream);
 }
 
 // Two keys per team per batch: with two 16-byte chunks per lane that keeps as many
