@@ -99,18 +99,29 @@ __device__ __forceinline__ float team_sum(float x)
     return x;
 }
 
+// max(a, b) of two scores as one v_med3(a, b, +inf). fmaxf keeps IEEE NaN quieting, so
+// the compiler first canonicalises every operand whose producer it cannot see through
+// (an MFMA result, a lane permute): one more instruction per operand. The two agree
+// on every non-NaN pair, -inf included.
+__device__ __forceinline__ float score_max(float a, float b)
+{
+    float inf = __builtin_huge_valf();
+    asm("" : "+v"(inf));   // opaque, so the med3 is not turned back into fmaxf
+    return __builtin_amdgcn_fmed3f(a, b, inf);
+}
+
 // Reductions over the lane pairs (l, l^16) and (l, l^32) with the gfx950 row-swap
 // permutes: both operands start as x, and after the swap one holds the partner rows.
 // VALU only (no trip through the LDS queue, unlike a lane shuffle).
 __device__ __forceinline__ float xor16_max(float x)
 {
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return score_max(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor32_max(float x)
 {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return score_max(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor16_sum(float x)
 {

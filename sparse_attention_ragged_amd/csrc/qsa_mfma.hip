@@ -270,10 +270,10 @@ gather_mfma_kernel(GatherParams p)
                 for (int i = 0; i < 4; ++i)
                     sc[h][i] = (present >> (16 * h + 4 * lq + i)) & 1u ? sc[h][i] : kNegInf;
         }
-        float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        float mx = score_max(score_max(score_max(sc[0][0], sc[0][1]), score_max(sc[0][2], sc[0][3])),
+                         score_max(score_max(sc[1][0], sc[1][1]), score_max(sc[1][2], sc[1][3])));
         mx = xor32_max(xor16_max(mx));
-        mx = fmaxf(fold ? mx * p.scale_log2 : mx, m);
+        mx = score_max(fold ? mx * p.scale_log2 : mx, m);
         if (__any(mx > m + kSlack)) {
             const float alpha = __builtin_amdgcn_exp2f(m - mx);
             lsum *= alpha;
