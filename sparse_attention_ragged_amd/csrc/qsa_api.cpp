@@ -300,6 +300,7 @@ qsa_status qsa_block_sparse_attention(void *out, const qsa_ragged_q *q, const qs
     p.cache_lengths = kv->cache_lengths;
     p.list_kind = KEYS_BLOCKS;
     p.block_size = (int32_t)block_size;
+    p.block_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctzll((unsigned long long)block_size) : -1;
     p.indices = d_indices;
     p.width = topk;
     return run(p, plan, stream);

@@ -271,6 +271,14 @@ __device__ __forceinline__ int64_t key_list_length(const GatherParams &p, int64_
 // wait for exactly the oldest batch. Entries at or past counts are never loaded.
 
 // Stage 1: address of key jj's list entry (or a dummy, whose value is not used).
+// Block of a block-sparse list slot jj (below 2^31: the host bounds topk * block_size
+// by 2^30): a shift for power-of-two block sizes, else a 32-bit division.
+__device__ __forceinline__ uint32_t block_of(const GatherParams &p, int64_t jj)
+{
+    const uint32_t j = (uint32_t)jj;
+    return p.block_shift >= 0 ? j >> p.block_shift : j / (uint32_t)p.block_size;
+}
+
 template <int LIST>
 __device__ __forceinline__ const int32_t *entry_ptr(const GatherParams &p, int64_t r, int g, int64_t jj,
                                                     bool present)
@@ -281,7 +289,7 @@ __device__ __forceinline__ const int32_t *entry_ptr(const GatherParams &p, int64
     if constexpr (LIST == KEYS_TOKEN_INDICES)
         return p.indices + r * p.width + jj;
     if constexpr (LIST == KEYS_BLOCKS)
-        return p.indices + ((int64_t)g * p.total_q + r) * p.width + jj / p.block_size;
+        return p.indices + ((int64_t)g * p.total_q + r) * p.width + block_of(p, jj);
     return jj < p.window ? dummy : p.indices + r * p.width + (jj - p.window);
 }
 
@@ -300,7 +308,7 @@ __device__ __forceinline__ KeyPos key_pos(const GatherParams &p, int64_t pos, in
     KeyPos k{raw, false, present};
     if constexpr (LIST == KEYS_BLOCKS) {
         const int32_t bs = p.block_size;
-        const int32_t t = (int32_t)jj / bs;
+        const int32_t t = (int32_t)block_of(p, jj);
         const int64_t tok = (int64_t)raw * bs + ((int32_t)jj - t * bs);
         k.present = present && raw >= 0 && tok <= pos;
         k.tok = (int32_t)tok;

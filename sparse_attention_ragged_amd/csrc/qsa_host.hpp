@@ -67,6 +67,7 @@ struct GatherParams {
     CacheAddr comp;                  // compressed leaf (latent only)
     int32_t list_kind;
     int32_t block_size;
+    int32_t block_shift;             // log2(block_size) when it is a power of two, else -1
     const int32_t *indices;          // token_indices / d_indices / comp_indices
     const int32_t *counts;           // token-index counts (KEYS_TOKEN_INDICES)
     int64_t width;                   // W, topk or num_comp

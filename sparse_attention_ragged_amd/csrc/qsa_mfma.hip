@@ -70,14 +70,20 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v)
     return r;
 }
 
-// 8 e4m3 codes -> 8 bf16 (exact: every e4m3 value is a bf16 value)
+// 8 e4m3 codes -> 8 bf16 (exact: every e4m3 value is a bf16 value), two codes per
+// gfx950 scaled conversion with a scale of 1
+template <bool HIGH>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w)
+{
+    const auto v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH);
+    uint32_t u;
+    __builtin_memcpy(&u, &v, sizeof u);
+    return u;
+}
 __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 w)
 {
-    float f[8];
-    e4m3x4_to_f32(w[0], f);
-    e4m3x4_to_f32(w[1], f + 4);
-    return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                 pack_bf16x2(f[6], f[7])};
+    return u32x4{e4m3x2_to_bf16x2<false>(w[0]), e4m3x2_to_bf16x2<true>(w[0]), e4m3x2_to_bf16x2<false>(w[1]),
+                 e4m3x2_to_bf16x2<true>(w[1])};
 }
 
 template <int DT, int D, int LIST>
@@ -144,16 +150,38 @@ gather_mfma_kernel(GatherParams p)
             qf[c] = head_real ? v : u32x2{0, 0};
         }
     }
+    const int64_t j0 = (int64_t)s * p.split_keys;
+    const int64_t jend = j0 + p.split_keys;
+    int64_t j1 = n < jend ? n : jend;            // dense: set once the row's sequence is known
+
+    // Lane l (and l + 32) walks key l % 32 of each tile through the address pipeline.
+    // The list entries do not depend on the row's sequence, so the first two tiles'
+    // entries are loaded before its lookup.
+    const int kl = lane & 31;
+    struct Entries { int32_t raw; };
+    auto key_index = [&](int batch) -> int64_t { return j0 + (int64_t)batch * kTileKeys + kl; };
+    auto load_entries = [&](int batch, Entries &E) {
+        const int64_t jj = key_index(batch);
+        if constexpr (LIST == KEYS_DENSE)
+            E.raw = 0;                             // dense: the key is its index, nothing to load
+        else
+            E.raw = *entry_ptr<LIST>(p, r, g, jj, jj < j1);
+    };
+    Entries E0, E1;
+    load_entries(0, E0);
+    load_entries(1, E1);
+
     int64_t pos = 0;
     const int b = find_seq_pos_wave(p.row_off,
                                     LIST == KEYS_TOKEN_INDICES || LIST == KEYS_DENSE ? nullptr : p.cache_lengths,
                                     p.batch, (uint32_t)r, pos);
-    if constexpr (LIST == KEYS_DENSE)
+    if constexpr (LIST == KEYS_DENSE) {
         n = dense_key_range(p, r, b, pos);     // pos: row index of the row's first key
-    const int64_t j0 = (int64_t)s * p.split_keys;
-    const int64_t jend = j0 + p.split_keys;
-    const int64_t j1 = n < jend ? n : jend;
-    const int nb = j1 > j0 ? (int)((j1 - j0 + kTileKeys - 1) / kTileKeys) : 0;
+        j1 = n < jend ? n : jend;
+    }
+    // the same in every lane; taken from lane 0 so the tile loop's exits are uniform
+    // branches and every trip of it starts with the same loads in flight
+    const int nb = __builtin_amdgcn_readfirstlane(j1 > j0 ? (int)((j1 - j0 + kTileKeys - 1) / kTileKeys) : 0);
     const int64_t vdelta = LIST == KEYS_LATENT  ? 0
                            : LIST == KEYS_DENSE ? static_cast<const char *>(p.dense_v) - static_cast<const char *>(p.dense_k)
                                                 : (int64_t)p.kv.plane_stride_b;
@@ -168,27 +196,16 @@ gather_mfma_kernel(GatherParams p)
     // the scale is applied once to the maximum and folded into the exponent's FMA
     const bool fold = p.scale_log2 > 0.f;
 
-    // Lane l (and l + 32) walks key l % 32 of each tile through the address pipeline
-    // and leaves the key's K and V row addresses in the wavefront's LDS; the rows are
-    // then loaded row-contiguous: load instruction i of a plane reads rows
+    // Each key's K and V row addresses go to the wavefront's LDS; the rows are then
+    // loaded row-contiguous: load instruction i of a plane reads rows
     // i*KPI .. i*KPI + KPI-1, LPK lanes per row, every lane reading its row's addresses
     // back from LDS (all reads in flight at once, one wait).
-    const int kl = lane & 31;
     const int my_row = lane / LPK;              // row within a load instruction
     const int my_chunk = lane % LPK;            // 16-byte chunk within the row
-    struct Entries { int32_t raw; };
     struct Pages { KeyPos k; int32_t slot; uint32_t page; };
     struct Rows { u32x4 k[NI], v[NI]; uint32_t present; };
     const int chunk_b = my_chunk * 16;
 
-    auto key_index = [&](int batch) -> int64_t { return j0 + (int64_t)batch * kTileKeys + kl; };
-    auto load_entries = [&](int batch, Entries &E) {
-        const int64_t jj = key_index(batch);
-        if constexpr (LIST == KEYS_DENSE)
-            E.raw = 0;                             // dense: the key is its index, nothing to load
-        else
-            E.raw = *entry_ptr<LIST>(p, r, g, jj, jj < j1);
-    };
     auto load_pages = [&](int batch, const Entries &E, Pages &P) {
         const int64_t jj = key_index(batch);
         P.k = key_pos<LIST>(p, pos, jj, E.raw, jj < j1);
@@ -205,8 +222,13 @@ gather_mfma_kernel(GatherParams p)
         R.present = (uint32_t)(__ballot(ok) & 0xffffffffull);
         // an absent key reads the q row for both planes (its weight is zero). The
         // previous tile's reads of these slots came earlier in this wavefront's LDS order.
-        if (lane < kTileKeys)
-            s_rows[kl] = u64x2{(uint64_t)(uintptr_t)a, (uint64_t)(uintptr_t)(ok ? a + vdelta : dummy)};
+        // Lanes l and l + 32 walk the same key and store the same pair (no branch). The
+        // empty asm statements tell the compiler that other lanes change these slots:
+        // without them it may take a lane to read back what it read the previous time
+        // (nothing it stored changed them) and reuse that load's rows.
+        asm volatile("" ::: "memory");
+        s_rows[kl] = u64x2{(uint64_t)(uintptr_t)a, (uint64_t)(uintptr_t)(ok ? a + vdelta : dummy)};
+        asm volatile("" ::: "memory");
         u64x2 e[NI];
 #pragma unroll
         for (int i = 0; i < NI; ++i)
@@ -317,11 +339,8 @@ gather_mfma_kernel(GatherParams p)
     // tile i is computed from LDS while they are in flight. Every trip starts with
     // entries i + 2, pages i + 1 and rows i in flight.
     if (nb > 0) {
-        Entries E0, E1;
         Pages P0, P1;
         Rows R;
-        load_entries(0, E0);
-        load_entries(1, E1);
         load_pages(0, E0, P0);
         load_entries(2, E0);
         load_pages(1, E1, P1);

@@ -83,6 +83,44 @@ def test_qsa_mfma_counts_one_exact():
         assert torch.equal(out[r].cpu().view(torch.int16), v.view(torch.int16)), (r, pos[r])
 
 
+def test_qsa_mfma_e4m3_values_exact_every_code():
+    """counts = 1 on the e4m3 matrix-core path returns the selected V row exactly, with
+    the V rows holding every finite e4m3 code between them: pins the kernel's e4m3 ->
+    bf16 widening of V (byte order and exactness) against torch's e4m3 decoding."""
+    case = prefill_small(seed=13, rows=(3, 2), cache=(40, 90), W_=16, g=8, d=128, dtype="e4m3", out="bf16")
+    c = copy.copy(case)
+    c.counts = np.ones_like(case.counts)
+    pv = case.kv.pages_view().view(torch.uint8)
+    H, ps = case.kv.num_kv_heads, case.kv.page_size
+    off = case.input_row_offsets
+    sel = []
+    for r in range(case.total_q):
+        b = int(np.searchsorted(off, r, side="right") - 1)
+        p = int(case.token_indices[r, 0])
+        sel.append((int(case.kv.lookup_table[b, p // ps]), p % ps))
+    # V rows of the selected keys, kv head g: codes (k * 128 + d) mod 256, the two NaN
+    # codes replaced by zero (distinct selections first, so every code appears)
+    distinct = sorted(set(sel))
+    assert len(distinct) * H * 128 >= 256
+    for k, (page, slot) in enumerate(distinct):
+        for g in range(H):
+            codes = (np.arange(128) + (k * H + g) * 128) % 256
+            codes[(codes == 0x7F) | (codes == 0xFF)] = 0
+            pv[page, 1, 0, slot, g] = torch.from_numpy(codes.astype(np.uint8))
+    announce("qsa mfma e4m3 counts=1, every finite code")
+    dc = D.to_device(c, DEV)
+    out = D.run(dc)
+    torch.cuda.synchronize()
+    G = case.num_q_heads // H
+    seen = set()
+    for r, (page, slot) in enumerate(sel):
+        raw = pv[page, 1, 0, slot]                                   # [H, D] codes
+        v = raw.view(torch.float8_e4m3fn).float().repeat_interleave(G, dim=0)
+        assert torch.equal(out[r].cpu().float(), v), r
+        seen.update(raw.flatten().tolist())
+    assert seen == set(range(256)) - {0x7F, 0xFF}
+
+
 def test_c3_prefill_full_size_all_rows():
     """The ragged-prefill workload at full size (8 sequences, ~9.7k rows, group 16) in
     the default launch configuration; the oracle checks every row."""
