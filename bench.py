@@ -197,7 +197,7 @@ def prepare(case, R, dev, opts):
     del dc
     torch.cuda.synchronize()
     ws_n = D.workspace_size(calls[0], opts)
-    ws = torch.zeros(max(ws_n, 16), dtype=torch.uint8, device=dev)   # zero-filled once (work counter)
+    ws = torch.zeros(max(ws_n, 16), dtype=torch.uint8, device=dev)   # zero-filled once
     out = torch.empty(tuple(case.q.shape), dtype=D.out_dtype(case), device=dev)
     return calls, ws, out
 

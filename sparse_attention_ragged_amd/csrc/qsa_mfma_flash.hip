@@ -116,7 +116,18 @@ gather_mfma_flash_kernel(GatherParams p)
         K0 = s_range[w][0] < K0 ? s_range[w][0] : K0;
         K1 = s_range[w][1] > K1 ? s_range[w][1] : K1;
     }
-    const int nt = K1 > K0 ? (int)((K1 - K0 + kFlashTile - 1) / kFlashTile) : 0;
+    // Row indices, key ranges and tile starts in 32 bits (total_q < 2^31 is checked on
+    // the host; a prefetched tile past the range stays below 2^32), each the same in
+    // every lane and taken from lane 0, so that the per-tile range tests are scalar.
+    const uint32_t K0u = K1 > K0 ? (uint32_t)__builtin_amdgcn_readfirstlane((int)K0) : 0u;
+    const uint32_t K1u = K1 > K0 ? (uint32_t)__builtin_amdgcn_readfirstlane((int)K1) : 0u;
+    const int nt = (int)((K1u - K0u + kFlashTile - 1) / kFlashTile);
+    uint32_t fu[RW], nu[RW];                     // each row's first key and key count
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+        fu[j] = (uint32_t)__builtin_amdgcn_readfirstlane((int)first[j]);
+        nu[j] = (uint32_t)__builtin_amdgcn_readfirstlane((int)n[j]);
+    }
 
     // softmax state per row: reference m (log2 units) of head li, the P.V accumulator
     // and the running sum of the weights, kept by an MFMA with an all-ones A operand
@@ -142,15 +153,16 @@ gather_mfma_flash_kernel(GatherParams p)
     const int my_chunk = lane % LPK;
     const char *kbase = static_cast<const char *>(p.dense_k) + ((int64_t)g * D) * EB + my_chunk * 16;
     const char *vbase = static_cast<const char *>(p.dense_v) + ((int64_t)g * D) * EB + my_chunk * 16;
-    const int64_t row_stride = (int64_t)p.num_kv_heads * D * EB;
+    const uint32_t row_stride = (uint32_t)p.num_kv_heads * D * EB;
     struct Rows { u32x4 k[NI], v[NI]; };
     auto load_tile = [&](int t, Rows &R) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int64_t kg = K0 + (int64_t)t * kFlashTile + RPW * wave + i * KPI + my_row;
-            const int64_t kr = kg < K1 ? kg : K0;          // past the range: a readable row
-            R.k[i] = ldg16(kbase + kr * row_stride);
-            R.v[i] = ldg16(vbase + kr * row_stride);
+            const uint32_t kg = K0u + (uint32_t)t * kFlashTile + (uint32_t)(RPW * wave + i * KPI + my_row);
+            const uint32_t kr = kg < K1u ? kg : K1u - 1;   // past the range: its last row (readable)
+            const uint64_t off = (uint64_t)kr * row_stride;
+            R.k[i] = ldg16(kbase + off);
+            R.v[i] = ldg16(vbase + off);
         }
     };
     auto store_tile = [&](int buf, const Rows &R) {
@@ -165,11 +177,11 @@ gather_mfma_flash_kernel(GatherParams p)
     };
     auto consume = [&](int t, int buf, auto fold_c) {
         constexpr bool fold = decltype(fold_c)::value;
-        const int64_t t0 = K0 + (int64_t)t * kFlashTile;
+        const uint32_t t0 = K0u + (uint32_t)t * kFlashTile;
         bool any = false;
 #pragma unroll
         for (int j = 0; j < RW; ++j)
-            any = any || (t0 < first[j] + n[j] && t0 + kFlashTile > first[j]);
+            any = any || (t0 < fu[j] + nu[j] && t0 + kFlashTile > fu[j]);
         if (!any)
             return;                               // no key of these rows in the tile
         const char *s_k = smem + buf * kBufBytes;
@@ -197,8 +209,8 @@ gather_mfma_flash_kernel(GatherParams p)
         for (int j = 0; j < RW; ++j) {
             // key index relative to the row's first key; a tile wholly inside the
             // row's range (all but its first and last few) needs no mask
-            const int64_t rel64 = t0 - first[j];
-            const bool whole = rel64 >= 0 && rel64 + kFlashTile <= n[j];
+            const int32_t rel0 = (int32_t)(t0 - fu[j]);
+            const bool whole = rel0 >= 0 && rel0 + kFlashTile <= (int32_t)nu[j];
             float sc[2][4];
 #pragma unroll
             for (int h = 0; h < 2; ++h)
@@ -206,8 +218,8 @@ gather_mfma_flash_kernel(GatherParams p)
                 for (int i = 0; i < 4; ++i)
                     sc[h][i] = fold ? st[j][h][i] : st[j][h][i] * p.scale_log2;
             if (!whole) {
-                const int32_t rel = (int32_t)(rel64 < -kFlashTile ? -kFlashTile : rel64 > n[j] ? n[j] : rel64);
-                const uint32_t nn = (uint32_t)n[j];
+                const int32_t rel = rel0 < -kFlashTile ? -kFlashTile : rel0 > (int32_t)nu[j] ? (int32_t)nu[j] : rel0;
+                const uint32_t nn = nu[j];
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
