@@ -58,14 +58,8 @@ template <> struct Elem<QSA_FP8_E4M3> { static constexpr int bytes = 1; };
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-// binary32 -> bf16 with round-to-nearest-even; NaN stays a (quiet) NaN. Branch-free.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
-{
-    const uint32_t u = __float_as_uint(f);
-    const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-    const uint32_t nan = (u >> 16) | 0x40u;
-    return (u & 0x7fffffffu) > 0x7f800000u ? nan : rne;
-}
+// binary32 -> bf16 bits, round to nearest even (the hardware conversion; NaN stays a NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
 // Four OCP E4M3 codes (one dword) -> four floats, exact, via the gfx950 converter.
 __device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float *o)
@@ -478,8 +472,7 @@ __device__ __forceinline__ void store_out4(void *out, int32_t out_dtype, int64_t
 {
     if (out_dtype == QSA_BF16) {
         typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
-        const u32x2v w = {f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
-                          f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16)};
+        const u32x2v w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         *reinterpret_cast<u32x2v *>(static_cast<uint16_t *>(out) + idx) = w;
     } else {
         *reinterpret_cast<f32x4_t *>(static_cast<float *>(out) + idx) = v;
@@ -490,8 +483,7 @@ __device__ __forceinline__ void store_out4(void *out, int32_t out_dtype, int64_t
 __device__ __forceinline__ void store_out2(void *out, int32_t out_dtype, int64_t idx, float v0, float v1)
 {
     if (out_dtype == QSA_BF16)
-        *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(out) + idx) =
-            f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+        *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(out) + idx) = pack_bf16x2(v0, v1);
     else
         *reinterpret_cast<float2 *>(static_cast<float *>(out) + idx) = make_float2(v0, v1);
 }

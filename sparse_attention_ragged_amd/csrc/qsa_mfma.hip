@@ -111,7 +111,7 @@ gather_mfma_kernel(GatherParams p)
     const int G = p.group;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: the item's indices follow
     const int NW = blockDim.x >> 6;
 
     // XCD-contiguous renumbering of the workgroups (blocks are dealt to the 8 XCDs
