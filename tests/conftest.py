@@ -10,7 +10,7 @@ if ROOT not in sys.path:
 # attention ops. Files not listed run after these, in their usual order.
 GPU_ORDER = ("test_gpu_qsa.py", "test_gpu_mfma.py", "test_gpu_latent.py", "test_gpu_graph.py",
              "test_gpu_dense.py", "test_gpu_compress.py", "test_gpu_select.py", "test_gpu_scale.py",
-             "test_gpu_batches.py")
+             "test_gpu_batches.py", "test_gpu_shapes.py")
 
 
 def pytest_configure(config):
