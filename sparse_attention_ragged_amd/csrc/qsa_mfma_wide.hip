@@ -113,13 +113,21 @@ gather_mfma_wide_kernel(GatherParams p)
 
     const bool is_score = wave >= kWaves;
     // normalised output rows of this wavefront's heads (one split) or the split's partial
-    auto finish = [&](float m, float lsum, const f32x4_t *acc) {
+    auto finish = [&](float m, float lsum, const f32x4_t *acc, float sink_l2) {
         const int64_t gh = (int64_t)head;       // the single kv head: group = all q heads
         if (!head_real)
             return;
         const int64_t rh = r * p.num_q_heads + gh;
         if (S == 1) {
-            const float inv = final_factor(p, gh, m, lsum);
+            float inv;
+            if (p.sink) {                       // the sink logit, loaded at the start
+                const float M2 = fmaxf(m, sink_l2);
+                const float c = __builtin_amdgcn_exp2f(m - M2);
+                const float L = lsum * c + __builtin_amdgcn_exp2f(sink_l2 - M2);
+                inv = L > 0.f ? c / L : 0.f;
+            } else {
+                inv = lsum > 0.f ? 1.f / lsum : 0.f;
+            }
 #pragma unroll
             for (int t = 0; t < NDT; ++t)
                 store_out4(p.out, p.out_dtype, rh * D + 16 * t + 4 * lq, acc[t] * inv);
@@ -140,7 +148,7 @@ gather_mfma_wide_kernel(GatherParams p)
 #pragma unroll
             for (int t = 0; t < NDT; ++t)
                 zero[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            finish(kNoKey, 0.f, zero);
+            finish(kNoKey, 0.f, zero, kNegInf);
         }
         return;
     }
@@ -319,6 +327,22 @@ gather_mfma_wide_kernel(GatherParams p)
         int32_t E[kDepth];
         Page P[kDepth];
         Rows R[kDepth];
+        // the score wavefronts' q rows and the value wavefronts' sink logit are loaded
+        // here, before the first barrier, so that their latency overlaps the dependent
+        // chain (list entries -> sequence -> page entries -> rows) of the first tile
+        // B operand of S^T: 8 dims of this lane's head per 32-dim chunk (zeros for padding heads)
+        u32x4 qf[NC];
+        float sink_l2 = kNegInf;
+        if (is_score) {
+            const char *qrow = qrow0 + (int64_t)(head_real ? head : 0) * D * EB;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const u32x4 v = ldg16(qrow + (32 * c + 8 * lq) * EB);
+                qf[c] = head_real ? v : u32x4{0, 0, 0, 0};
+            }
+        } else if (p.sink) {
+            sink_l2 = p.sink[head_real ? head : 0] * 1.44269504088896340736f;
+        }
         if (!is_score) {
             int32_t e_fill[3 * kDepth + 1];
 #pragma unroll
@@ -372,14 +396,6 @@ gather_mfma_wide_kernel(GatherParams p)
             }
         };
         if (is_score) {
-            // B operand of S^T: 8 dims of this lane's head per 32-dim chunk (zeros for padding heads)
-            const char *qrow = qrow0 + (int64_t)(head_real ? head : 0) * D * EB;
-            u32x4 qf[NC];
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const u32x4 v = ldg16(qrow + (32 * c + 8 * lq) * EB);
-                qf[c] = head_real ? v : u32x4{0, 0, 0, 0};
-            }
             float m = kNoKey;
             steps([&](int tt, int u) {
                 if (tt < nb)
@@ -399,7 +415,7 @@ gather_mfma_wide_kernel(GatherParams p)
                 accumulate(tt - 1, (u + kXBufs - 1) % kXBufs, acc, lsum);
         });
         lds_barrier();                          // the score wavefronts' final reference
-        finish(s_m[hw][li], lsum[0], acc);
+        finish(s_m[hw][li], lsum[0], acc, sink_l2);
     }
 }
 
