@@ -32,6 +32,8 @@
 // split, in the combine kernel otherwise).
 #include "qsa_device.hpp"
 
+#include <type_traits>
+
 namespace qsa {
 
 namespace {
@@ -139,6 +141,72 @@ gather_mfma_wide_kernel(GatherParams p)
             if (lq == 0) {
                 p.ws_ml[srh * 2] = m;
                 p.ws_ml[srh * 2 + 1] = lsum;
+            }
+        }
+    };
+    // The same, once every key tile is consumed: in the MFMA layout a lane holds four
+    // positions of one head, so a direct store writes 32-byte pieces of 16 rows per
+    // instruction (measured: about 7700 cycles for a 64-head row of D 512, most of a
+    // workgroup's epilogue). Instead the values pass through this wavefront's own eight
+    // rows of key tile 0 (16 heads x D bytes, rows padded by 16 bytes) so that every
+    // store writes whole 16-byte chunks of one row, D bytes of a head per pass (two
+    // passes of bf16, four of fp32).
+    auto finish_staged = [&](float m, float lsum, const f32x4_t *acc, float sink_l2) {
+        constexpr int RS = D + 16;              // bytes per head in the staging rows
+        constexpr int CPR = D / 16;             // 16-byte chunks per head and pass
+        char *stage = reinterpret_cast<char *>(s_x[0] + 8 * hw * ROW);
+        float scale = 1.f;
+        if (S == 1) {
+            if (p.sink) {                       // the sink logit, loaded at the start
+                const float M2 = fmaxf(m, sink_l2);
+                const float c = __builtin_amdgcn_exp2f(m - M2);
+                const float L = lsum * c + __builtin_amdgcn_exp2f(sink_l2 - M2);
+                scale = L > 0.f ? c / L : 0.f;
+            } else {
+                scale = lsum > 0.f ? 1.f / lsum : 0.f;
+            }
+        }
+        auto emit = [&](auto ob, char *dst0, int64_t row_bytes) {
+            constexpr int OB = decltype(ob)::value;
+            constexpr int PT = D / OB / 16;     // MFMA tiles per pass
+#pragma unroll
+            for (int pass = 0; pass < OB; ++pass) {
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int tl = 0; tl < PT; ++tl) {
+                    const f32x4_t v = acc[pass * PT + tl] * scale;
+                    char *a = stage + li * RS + (16 * tl + 4 * lq) * OB;
+                    if constexpr (OB == 2) {
+                        typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+                        *reinterpret_cast<u32x2v *>(a) = u32x2v{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                    } else {
+                        *reinterpret_cast<f32x4_t *>(a) = v;
+                    }
+                }
+                asm volatile("" ::: "memory");  // the reads below take other lanes' values
+#pragma unroll
+                for (int j = 0; j < D / 64; ++j) {
+                    const int c = j * 64 + lane;
+                    const int hh = c / CPR, q = c % CPR;
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + hh * RS + q * 16);
+                    if (16 * hw + hh < G)
+                        *reinterpret_cast<u32x4 *>(dst0 + (int64_t)hh * row_bytes + pass * D + q * 16) = v;
+                }
+            }
+        };
+        if (S == 1) {
+            const int eb = p.out_dtype == QSA_BF16 ? 2 : 4;
+            char *dst0 = static_cast<char *>(p.out) + (r * p.num_q_heads + 16 * hw) * (int64_t)D * eb;
+            if (p.out_dtype == QSA_BF16)
+                emit(std::integral_constant<int, 2>{}, dst0, (int64_t)D * 2);
+            else
+                emit(std::integral_constant<int, 4>{}, dst0, (int64_t)D * 4);
+        } else {
+            const int64_t srh0 = ((int64_t)s * (p.total_q - R0) + (r - R0)) * p.num_q_heads + 16 * hw;
+            emit(std::integral_constant<int, 4>{}, reinterpret_cast<char *>(p.ws_acc + srh0 * D), (int64_t)D * 4);
+            if (lq == 0 && head_real) {
+                p.ws_ml[(srh0 + li) * 2] = m;
+                p.ws_ml[(srh0 + li) * 2 + 1] = lsum;
             }
         }
     };
@@ -414,8 +482,8 @@ gather_mfma_wide_kernel(GatherParams p)
             if (tt >= 1 && tt <= nb)
                 accumulate(tt - 1, (u + kXBufs - 1) % kXBufs, acc, lsum);
         });
-        lds_barrier();                          // the score wavefronts' final reference
-        finish(s_m[hw][li], lsum[0], acc, sink_l2);
+        lds_barrier();                          // the score wavefronts' final reference; tiles consumed
+        finish_staged(s_m[hw][li], lsum[0], acc, sink_l2);
     }
 }
 
