@@ -363,25 +363,64 @@ gather_mfma_kernel(GatherParams p)
         }
     }
 
-    // per-head sum over the four lanes of each head; lane (i, q) then stores dims
-    // 16t + 4q .. 16t + 4q + 3 of head i
+    // Per-head sum over the four lanes of each head. Lane (i, q) holds dims 16t + 4q ..
+    // 16t + 4q + 3 of head i, so a direct store would write 32- or 64-byte pieces of up
+    // to 16 rows per instruction; the values pass through this wavefront's own LDS
+    // region (free after its last tile; 16 head slots x D bytes, padded by 16) so that
+    // every store writes whole 16-byte chunks of one row, D bytes of a head per pass
+    // (two passes of bf16, four of fp32).
     lsum = xor32_sum(xor16_sum(lsum));
-    if (li < G) {
-        const int64_t head = (int64_t)g * G + li;
-        const int64_t rh = r * p.num_q_heads + head;
+    {
+        constexpr int RS = D + 16;              // staging bytes per head slot
+        constexpr int CPR = D / 16;             // 16-byte chunks per head and pass
+        static_assert(16 * RS <= kWaveLds, "the staging rows fit the wavefront's LDS region");
+        static_assert(D % 64 == 0, "whole wavefront stores");
+        char *stage = s_k;
+        const int64_t head0 = (int64_t)g * G;   // this kv head's first q head
+        float scale = 1.f;
+        if (S == 1 && li < G)
+            scale = final_factor(p, head0 + li, m, lsum);
+        auto emit = [&](auto ob, char *dst0, int64_t row_bytes) {
+            constexpr int OB = decltype(ob)::value;
+            constexpr int PT = D / OB / 16;     // MFMA tiles per pass
+#pragma unroll
+            for (int pass = 0; pass < OB; ++pass) {
+                asm volatile("" ::: "memory");  // after the last tile's reads of this region
+#pragma unroll
+                for (int tl = 0; tl < PT; ++tl) {
+                    const f32x4_t v = acc[pass * PT + tl] * scale;
+                    char *a = stage + li * RS + (16 * tl + 4 * lq) * OB;
+                    if constexpr (OB == 2) {
+                        typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+                        *reinterpret_cast<u32x2v *>(a) = u32x2v{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                    } else {
+                        *reinterpret_cast<f32x4_t *>(a) = v;
+                    }
+                }
+                asm volatile("" ::: "memory");  // the reads below take other lanes' values
+#pragma unroll
+                for (int j = 0; j < D / 64; ++j) {
+                    const int c = j * 64 + lane;
+                    const int hh = c / CPR, q = c % CPR;
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + hh * RS + q * 16);
+                    if (hh < G)
+                        *reinterpret_cast<u32x4 *>(dst0 + (int64_t)hh * row_bytes + pass * D + q * 16) = v;
+                }
+            }
+        };
         if (S == 1) {
-            const float f = final_factor(p, head, m, lsum);
-#pragma unroll
-            for (int t = 0; t < NDT; ++t)
-                store_out4(p.out, p.out_dtype, rh * D + 16 * t + 4 * lq, acc[t] * f);
+            const int eb = p.out_dtype == QSA_BF16 ? 2 : 4;
+            char *dst0 = static_cast<char *>(p.out) + (r * p.num_q_heads + head0) * (int64_t)D * eb;
+            if (p.out_dtype == QSA_BF16)
+                emit(std::integral_constant<int, 2>{}, dst0, (int64_t)D * 2);
+            else
+                emit(std::integral_constant<int, 4>{}, dst0, (int64_t)D * 4);
         } else {
-            const int64_t srh = (int64_t)s * p.total_q * p.num_q_heads + rh;
-#pragma unroll
-            for (int t = 0; t < NDT; ++t)
-                *reinterpret_cast<f32x4_t *>(p.ws_acc + srh * D + 16 * t + 4 * lq) = acc[t];
-            if (lq == 0) {
-                p.ws_ml[srh * 2] = m;
-                p.ws_ml[srh * 2 + 1] = lsum;
+            const int64_t srh0 = (int64_t)s * p.total_q * p.num_q_heads + r * p.num_q_heads + head0;
+            emit(std::integral_constant<int, 4>{}, reinterpret_cast<char *>(p.ws_acc + srh0 * D), (int64_t)D * 4);
+            if (lq == 0 && li < G) {
+                p.ws_ml[(srh0 + li) * 2] = m;
+                p.ws_ml[(srh0 + li) * 2 + 1] = lsum;
             }
         }
     }
