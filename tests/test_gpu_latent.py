@@ -35,7 +35,8 @@ def run(case, options=None, rows=None):
 
 
 @pytest.mark.parametrize("heads,d,out", [(64, 512, "bf16"), (64, 512, "f32"), (32, 256, "f32"), (48, 128, "f32"),
-                                         (40, 256, "f32"), (20, 512, "bf16"), (17, 128, "f32"),
+                                         (40, 256, "f32"), (20, 512, "bf16"), (17, 128, "f32"), (33, 128, "bf16"),
+                                         (48, 256, "bf16"),
                                          (16, 128, "f32"), (8, 256, "bf16"), (4, 128, "f32"), (2, 64, "f32")])
 def test_latent_shapes(heads, d, out):
     case = latent_small(heads=heads, d=d, out=out)

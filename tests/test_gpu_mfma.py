@@ -34,7 +34,7 @@ def prefill_small(seed=3, rows=(40, 7, 70), cache=(300, 0, 900), g=16, d=128, W_
 
 
 @pytest.mark.parametrize("g,d,out", [(16, 128, "bf16"), (16, 128, "f32"), (8, 128, "f32"), (16, 64, "f32"),
-                                     (12, 256, "f32")])
+                                     (12, 256, "f32"), (12, 64, "bf16"), (8, 256, "bf16")])
 def test_qsa_mfma_shapes(g, d, out):
     case = prefill_small(g=g, d=d, out=out)
     announce("qsa mfma g=%d d=%d out=%s" % (g, d, out))
