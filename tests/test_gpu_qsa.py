@@ -38,7 +38,7 @@ def test_c1_tiny_fp32():
     compare(got, ref, "f32", "c1")
 
 
-@pytest.mark.parametrize("splits", [1, 2, 3, 7, 16])
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 9, 12, 16, 17])
 def test_c1_split_counts(splits):
     case = W.c1_tiny_fp32()
     announce("c1 splits=%d" % splits)
