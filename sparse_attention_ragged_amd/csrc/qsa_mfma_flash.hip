@@ -300,18 +300,57 @@ gather_mfma_flash_kernel(GatherParams p)
             tiles(std::false_type());
     }
 
-    // per-head sums over the four lanes of each head; lane (i, q) stores dims
-    // 16u + 4q .. 16u + 4q + 3 of head i
+    // Per-head sums over the four lanes of each head. Lane (i, q) holds dims 16u + 4q ..
+    // 16u + 4q + 3 of head i, so a direct store would write 32- or 64-byte pieces of up to
+    // 16 rows per instruction; each row's values pass through this wavefront's own part
+    // of LDS tile buffer 0 (16 head slots x D bytes, padded by 16), which nobody reads
+    // after the tile loop's last barrier, so that every store writes whole 16-byte chunks
+    // of one output row, D bytes of a head per pass (two passes of bf16, four of fp32).
+    {
+        constexpr int RS = D + 16;              // staging bytes per head slot
+        constexpr int CPR = D / 16;             // 16-byte chunks per head and pass
+        static_assert(kFlashWaves * 16 * RS <= kBufBytes, "the staging rows fit tile buffer 0");
+        static_assert(D % 64 == 0, "whole wavefront stores");
+        char *stage = smem + wave * 16 * RS;
 #pragma unroll
-    for (int j = 0; j < RW; ++j) {
-        const float ls = lsum[j][0];
-        if (row_real[j] && li < G) {
-            const int64_t head = (int64_t)g * G + li;
-            const int64_t rh = (r0 + RW * wave + j) * p.num_q_heads + head;
-            const float f = final_factor(p, head, m[j], ls);
+        for (int j = 0; j < RW; ++j) {
+            const float ls = lsum[j][0];
+            const int64_t head0 = (int64_t)g * G;
+            const float f = li < G ? final_factor(p, head0 + li, m[j], ls) : 0.f;
+            const int64_t row = r0 + RW * wave + j;
+            auto emit = [&](auto ob) {
+                constexpr int OB = decltype(ob)::value;
+                constexpr int PT = D / OB / 16;     // MFMA tiles per pass
+                char *dst0 = static_cast<char *>(p.out) + (row * p.num_q_heads + head0) * (int64_t)D * OB;
 #pragma unroll
-            for (int u = 0; u < NDT; ++u)
-                store_out4(p.out, p.out_dtype, rh * D + 16 * u + 4 * lq, acc[j][u] * f);
+                for (int pass = 0; pass < OB; ++pass) {
+                    asm volatile("" ::: "memory");  // after the previous reads of this region
+#pragma unroll
+                    for (int tl = 0; tl < PT; ++tl) {
+                        const f32x4_t v = acc[j][pass * PT + tl] * f;
+                        char *a = stage + li * RS + (16 * tl + 4 * lq) * OB;
+                        if constexpr (OB == 2) {
+                            typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+                            *reinterpret_cast<u32x2v *>(a) = u32x2v{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                        } else {
+                            *reinterpret_cast<f32x4_t *>(a) = v;
+                        }
+                    }
+                    asm volatile("" ::: "memory");  // the reads below take other lanes' values
+#pragma unroll
+                    for (int q4 = 0; q4 < D / 64; ++q4) {
+                        const int c = q4 * 64 + lane;
+                        const int hh = c / CPR, q = c % CPR;
+                        const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + hh * RS + q * 16);
+                        if (row_real[j] && hh < G)
+                            *reinterpret_cast<u32x4 *>(dst0 + (int64_t)hh * D * OB + pass * D + q * 16) = v;
+                    }
+                }
+            };
+            if (p.out_dtype == QSA_BF16)
+                emit(std::integral_constant<int, 2>{});
+            else
+                emit(std::integral_constant<int, 4>{});
         }
     }
 }
