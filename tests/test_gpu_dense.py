@@ -106,3 +106,13 @@ def test_dense_per_row_kernel_matches_shared_tiles():
     got_rows, _, _ = run(case, options={"waves": 4})
     compare(got_auto, ref, "bf16", "dense shared tiles")
     compare(got_rows, ref, "bf16", "dense per-row")
+
+
+@pytest.mark.parametrize("g,d", [(16, 64), (12, 128), (16, 256)])
+def test_dense_shared_tiles_bf16_output(g, d):
+    """bf16 output rows of the shared-tile kernel at every head_dim it is built for, with
+    a group that leaves head slots of the 16-wide operand unused (group 12)."""
+    case = dense(87 + d, [150, 7, 64, 1, 90], 2, g, d, "bf16", out="bf16", causal=True)
+    announce("dense shared tiles bf16 out g=%d d=%d" % (g, d))
+    got, ref, _ = run(case)
+    compare(got, ref, "bf16", "dense bf16 out g=%d d=%d" % (g, d))
